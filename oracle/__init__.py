@@ -1,0 +1,31 @@
+"""CPU oracle for the DSA hot path (index scores, top-k selection, sparse
+MQA attention), in float64 from the definitions on the pages.
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything in
+this package.  It shares no code, header, table or helper with the HIP
+library (``long_context_02_amd``) and imports nothing from it.
+
+Parity status of each function (pins live in ``tests/test_oracle_*.py``):
+  fp8.e4m3_decode / e4m3_encode   pinned (torch's e4m3fn cast, exhaustive)
+  index_scores                    pinned (hand 4-token example, integer dot
+                                  identity, pure-Python brute force)
+  topk_select                     pinned (full sort by (score desc, index asc),
+                                  hand example, constructed ties)
+  sparse_mqa_attention            pinned (k >= L equals dense causal attention
+                                  from torch SDPA; q = 0 mean; single index;
+                                  permutation and duplicate closed forms)
+  dsa_forward                     pinned (composition; chunked prefill equals
+                                  the tail rows of a full prefill)
+"""
+from .fp8 import e4m3_decode, e4m3_encode, dequantize, E4M3_MAX  # noqa: F401
+from .dsa import (  # noqa: F401
+    index_scores,
+    index_scores_row,
+    topk_select,
+    topk_select_row,
+    sparse_mqa_attention,
+    sparse_mqa_attention_row,
+    dsa_forward,
+    default_sm_scale,
+)

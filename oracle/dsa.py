@@ -1,0 +1,248 @@
+"""Plain CPU oracle for DeepSeek Sparse Attention (DSA): index scores, top-k
+token selection and sparse MLA attention in MQA mode.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything
+under ``oracle/``.  The product path (the HIP library and its Python binding)
+never routes through this code, and this code imports nothing from it.
+
+Everything is computed in float64, one query row at a time, straight from the
+definitions on the pages:
+
+* index score (page "Paper Breakdown: DeepSeek-V3.2", section 2 "Architecture:
+  DSA (§2.1)", the index-score formula):
+      I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
+  with one indexer key k[s] per token shared by all indexer heads j (the
+  formula puts no head index on k);
+* token selection (same section, the attention formula): query t attends to
+  the latent entries c_s whose score is among the top-k of row I[t,:]; the
+  candidates are the earlier tokens and t itself ("DeepSeek V3.2: Sparse
+  Attention and Reinforcement Learning Updates", Summary: the selector keeps
+  only high-scoring past tokens);
+* sparse attention in MLA's MQA mode (page 1, "DSA under MLA (MQA Mode)"):
+  one latent vector per selected token is shared by every query head; the key
+  is the whole latent+rope vector, the value is its leading d_v latent part.
+
+Readings of points the pages leave open (each also listed in the design doc):
+inclusive causal boundary s <= q_offset + t; fewer than k candidates select
+all of them and pad with -1; ties go to the lower index; indices come out
+ascending; NaN ranks below every number; -0 equals +0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .fp8 import dequantize
+
+
+# --------------------------------------------------------------------------
+# Lightning indexer
+
+
+def _as_f64_tokens(x, scale):
+    """Indexer operand as float64: FP8 codes times per-row scale, or raw floats."""
+    x = np.asarray(x)
+    if x.dtype == np.uint8:
+        if scale is None:
+            raise ValueError("FP8 codes need a scale")
+        return dequantize(x, scale)
+    return x.astype(np.float64)
+
+
+def index_scores_row(q_row, w_row, K, n_cand):
+    """One row of the index-score matrix.
+
+    q_row : [H_I, d_I] float64 indexer queries of token t (one per head j)
+    w_row : [H_I]      float64 head weights w[t,j]
+    K     : [N, d_I]   float64 indexer keys k[s]
+    n_cand: number of candidates, q_offset + t + 1 capped at N
+
+    Returns I[t, 0:N] with -inf at s >= n_cand (outside the causal set).
+    Follows the index-score formula of page 1, section 2 "Architecture: DSA
+    (§2.1)": the sum over heads of w[t,j] * ReLU(q[t,j] . k[s]).
+    """
+    N = K.shape[0]
+    out = np.full(N, -np.inf)
+    if n_cand <= 0:
+        return out
+    D = q_row @ K[:n_cand].T  # [H_I, n_cand]; q[t,j] . k[s]
+    out[:n_cand] = w_row @ np.maximum(D, 0.0)  # sum_j w[t,j] * ReLU(.)
+    return out
+
+
+def index_scores(q_idx, k_idx, w, q_offset, q_scale=None, k_scale=None, rows=None):
+    """Index scores I[b,t,s] for the query rows ``rows`` (default: all).
+
+    q_idx [B,T,H_I,d_I] (uint8 e4m3fn codes with q_scale [B,T,H_I], or floats),
+    k_idx [B,N,d_I]     (uint8 codes with k_scale [B,N], or floats),
+    w     [B,T,H_I]     float weights.
+    Query t sits at absolute position q_offset + t and sees keys 0..q_offset+t.
+    Returns float64 [len(rows), N] when ``rows`` is a list of (b, t), else
+    [B, T, N].
+    """
+    q_idx = np.asarray(q_idx)
+    B, T = q_idx.shape[:2]
+    N = np.asarray(k_idx).shape[1]
+    w = np.asarray(w, dtype=np.float64)
+    full = rows is None
+    if full:
+        rows = [(b, t) for b in range(B) for t in range(T)]
+    out = np.empty((len(rows), N))
+    keys = {}
+    for r, (b, t) in enumerate(rows):
+        if b not in keys:
+            keys = {b: _as_f64_tokens(np.asarray(k_idx)[b],
+                                      None if k_scale is None else np.asarray(k_scale)[b])}
+        qs = None if q_scale is None else np.asarray(q_scale)[b, t]
+        q_row = _as_f64_tokens(q_idx[b, t], qs)
+        n_cand = min(N, q_offset + t + 1)
+        out[r] = index_scores_row(q_row, w[b, t], keys[b], n_cand)
+    return out.reshape(B, T, N) if full else out
+
+
+# --------------------------------------------------------------------------
+# Token selector
+
+
+def topk_select_row(scores_row, k, n_cand):
+    """Top-k token selection over the candidates 0..n_cand-1 of one score row.
+
+    Page 1, section 2 "Architecture: DSA (§2.1)": query t keeps the tokens s
+    whose score I[t,s] is among the top-k of I[t,:].  With fewer than k
+    candidates all of them are kept.  Among equal scores the lower index is
+    kept; NaN scores rank below every number.  The kept indices are returned
+    in ascending order and padded with -1 to length k.
+    """
+    v = np.asarray(scores_row, dtype=np.float64)[:n_cand]
+    n = min(k, n_cand)
+    out = np.full(k, -1, dtype=np.int64)
+    if n <= 0:
+        return out
+    finite_or_inf = ~np.isnan(v)
+    real = np.flatnonzero(finite_or_inf)
+    if real.size <= n:
+        # every non-NaN candidate is kept; the rest are the lowest-index NaNs
+        nan_idx = np.flatnonzero(~finite_or_inf)[: n - real.size]
+        keep = np.sort(np.concatenate([real, nan_idx]))
+    else:
+        vals = v[real]
+        # threshold: the n-th largest value
+        thr = np.partition(vals, vals.size - n)[vals.size - n]
+        above = real[vals > thr]
+        ties = real[vals == thr]  # ascending index order
+        keep = np.sort(np.concatenate([above, ties[: n - above.size]]))
+    out[: keep.size] = keep
+    return out
+
+
+def topk_select(scores, k, q_offset, rows=None):
+    """Top-k selection for every row of a [B,T,N] score tensor (or ``rows``).
+
+    ``scores`` may also be a [len(rows), N] array when ``rows`` is given; row
+    r then belongs to query (b, t) = rows[r].
+    """
+    scores = np.asarray(scores)
+    if rows is None:
+        B, T, N = scores.shape
+        out = np.empty((B, T, k), dtype=np.int64)
+        for b in range(B):
+            for t in range(T):
+                out[b, t] = topk_select_row(scores[b, t], k, min(N, q_offset + t + 1))
+        return out
+    N = scores.shape[-1]
+    out = np.empty((len(rows), k), dtype=np.int64)
+    for r, (b, t) in enumerate(rows):
+        row = scores[r] if scores.ndim == 2 else scores[b, t]
+        out[r] = topk_select_row(row, k, min(N, q_offset + t + 1))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Sparse MLA attention, MQA mode
+
+
+def sparse_mqa_attention_row(q_row, kv, idx_row, d_v, sm_scale):
+    """Attention of one query token over its selected latent entries.
+
+    q_row  : [H, d_qk] per-head queries in the latent(+rope) space
+    kv     : [N, d_qk] latent entries c_s, shared by all H heads (MQA mode)
+    idx_row: [k] selected token indices, -1 (or anything outside [0, N)) is an
+             empty slot; duplicates count as often as they appear
+    Returns (o [H, d_v], lse [H]).  With no valid index o = 0, lse = -inf.
+
+    Page 1, section 2: u_t = Attn(h_t, {c_s : I[t,s] in Top-k(I[t,:])}), with
+    "DSA under MLA (MQA Mode)": every head scores the same latent vector c_s;
+    the value is the leading d_v (latent) part of c_s.
+    """
+    N = kv.shape[0]
+    idx_row = np.asarray(idx_row)
+    sel = idx_row[(idx_row >= 0) & (idx_row < N)]
+    H = q_row.shape[0]
+    if sel.size == 0:
+        return np.zeros((H, d_v)), np.full(H, -np.inf)
+    C = kv[sel]                                  # [k', d_qk]
+    z = sm_scale * (q_row @ C.T)                 # [H, k'] logits
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ C[:, :d_v]) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def sparse_mqa_attention(q, kv, idx, d_v, sm_scale, rows=None):
+    """Sparse MQA attention for all query rows (or the (b, t) list ``rows``).
+
+    q [B,T,H,d_qk], kv [B,N,d_qk], idx [B,T,k] (or [len(rows), k] with rows).
+    Inputs are converted to float64 exactly (bf16 and fp32 both embed).
+    Returns (out, lse): [B,T,H,d_v], [B,T,H] or [R,H,d_v], [R,H].
+    """
+    q = np.asarray(q)
+    kv = np.asarray(kv)
+    idx = np.asarray(idx)
+    B, T, H, _ = q.shape
+    full = rows is None
+    if full:
+        rows = [(b, t) for b in range(B) for t in range(T)]
+    out = np.empty((len(rows), H, d_v))
+    lse = np.empty((len(rows), H))
+    cache = {}
+    for r, (b, t) in enumerate(rows):
+        if b not in cache:
+            cache = {b: kv[b].astype(np.float64)}
+        irow = idx[b, t] if (full or idx.ndim == 3) else idx[r]
+        out[r], lse[r] = sparse_mqa_attention_row(
+            q[b, t].astype(np.float64), cache[b], irow, d_v, sm_scale)
+    if full:
+        return out.reshape(B, T, H, d_v), lse.reshape(B, T, H)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# The whole path
+
+
+def dsa_forward(q_idx, k_idx, w, q, kv, *, k, q_offset, d_v, sm_scale,
+                q_scale=None, k_scale=None, rows=None):
+    """Index scores -> top-k selection -> sparse MQA attention.
+
+    Page 1, section 2 "Architecture: DSA (§2.1)": the indexer scores every
+    earlier token, the selector keeps the top-k per query, and attention runs
+    over the kept latent entries only.  Returns a dict with ``scores``,
+    ``idx``, ``out`` and ``lse`` (restricted to ``rows`` when given).
+    """
+    B, T = np.asarray(q_idx).shape[:2]
+    if rows is None:
+        rows = [(b, t) for b in range(B) for t in range(T)]
+    scores = index_scores(q_idx, k_idx, w, q_offset, q_scale=q_scale,
+                          k_scale=k_scale, rows=rows)
+    idx = topk_select(scores, k, q_offset, rows=rows)
+    out, lse = sparse_mqa_attention(q, kv, idx, d_v, sm_scale, rows=rows)
+    return {"scores": scores, "idx": idx, "out": out, "lse": lse, "rows": rows}
+
+
+def default_sm_scale(d_qk: int) -> float:
+    """Softmax scale 1/sqrt(d_qk) (the rule the small fp32 workload states)."""
+    return 1.0 / math.sqrt(d_qk)

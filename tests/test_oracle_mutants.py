@@ -1,0 +1,114 @@
+"""The oracle's pins must catch plausible mistakes.  Each case plants one
+mistake in the oracle (on the CPU, via monkeypatch) and checks that at least
+one pin then fails."""
+import numpy as np
+import pytest
+
+import oracle.dsa as od
+import oracle.fp8 as of
+import test_oracle_attn as ta
+import test_oracle_forward as tf
+import test_oracle_fp8 as t8
+import test_oracle_indexer as ti
+import test_oracle_topk as tt
+
+
+def _fails(pins, golden_dir):
+    for pin in pins:
+        try:
+            if "golden_dir" in pin.__code__.co_varnames[: pin.__code__.co_argcount]:
+                pin(golden_dir)
+            else:
+                pin()
+        except (AssertionError, IndexError, ValueError):
+            return True
+    return False
+
+
+INDEXER_PINS = [ti.test_hand_example_exact, ti.test_fp8_dot_equals_integer_dot,
+                ti.test_brute_force_python_loops, ti.test_scales_fold_through_relu]
+TOPK_PINS = [tt.test_bruteforce_many_seeds, tt.test_hand_example, tt.test_zero_ties_lower_index_wins,
+             tt.test_causal_range_and_padding]
+ATTN_PINS = [ta.test_k_ge_L_equals_dense_causal, ta.test_zero_query_gives_mean_of_values,
+             ta.test_single_index_gives_that_value_row, ta.test_permutation_invariance_and_duplicates]
+FWD_PINS = [tf.test_chunked_prefill_equals_tail_of_full_prefill, tf.test_forward_with_k_ge_L_is_dense_causal]
+
+
+def _no_relu(q_row, w_row, K, n_cand):
+    out = np.full(K.shape[0], -np.inf)
+    out[:n_cand] = w_row @ (q_row @ K[:n_cand].T)
+    return out
+
+
+def _causal_off_by_one(q_row, w_row, K, n_cand):
+    return _ORIG_ROW(q_row, w_row, K, min(K.shape[0], n_cand + 1))
+
+
+def _weights_after_sum(q_row, w_row, K, n_cand):
+    out = np.full(K.shape[0], -np.inf)
+    out[:n_cand] = w_row.sum() * np.maximum(q_row @ K[:n_cand].T, 0).mean(0)
+    return out
+
+
+_ORIG_ROW = od.index_scores_row
+_ORIG_TOPK = od.topk_select_row
+_ORIG_ATT = od.sparse_mqa_attention_row
+
+
+def _ties_to_higher(row, k, n_cand):
+    r = np.asarray(row, float)[:n_cand][::-1]
+    sel = _ORIG_TOPK(r, k, n_cand)
+    m = sel >= 0
+    sel[m] = n_cand - 1 - sel[m]
+    keep = np.sort(sel[m])
+    out = np.full(k, -1)
+    out[: keep.size] = keep
+    return out
+
+
+def _strict_past(row, k, n_cand):
+    return _ORIG_TOPK(row, k, n_cand - 1)
+
+
+def _value_from_tail(q_row, kv, idx_row, d_v, sm_scale):
+    kv2 = np.concatenate([kv[:, d_v:], kv[:, :d_v]], axis=1)[:, : kv.shape[1]]
+    o, _ = _ORIG_ATT(q_row, kv2, idx_row, d_v, sm_scale)
+    _, lse = _ORIG_ATT(q_row, kv, idx_row, d_v, sm_scale)
+    return o, lse
+
+
+def _no_scale(q_row, kv, idx_row, d_v, sm_scale):
+    return _ORIG_ATT(q_row, kv, idx_row, d_v, 1.0)
+
+
+def _drop_duplicates(q_row, kv, idx_row, d_v, sm_scale):
+    return _ORIG_ATT(q_row, kv, np.unique(np.asarray(idx_row)), d_v, sm_scale)
+
+
+@pytest.mark.parametrize("mutant", [_no_relu, _causal_off_by_one, _weights_after_sum])
+def test_indexer_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(od, "index_scores_row", mutant)
+    assert _fails(INDEXER_PINS + FWD_PINS, golden_dir)
+
+
+def test_dequant_scale_mutant_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(od, "dequantize", lambda c, s: of.e4m3_decode(c) * np.sqrt(np.asarray(s))[..., None])
+    assert _fails(INDEXER_PINS, golden_dir)
+
+
+def test_decode_bias_mutant_caught(monkeypatch, golden_dir):
+    orig = of.e4m3_decode
+    monkeypatch.setattr(t8, "e4m3_decode", lambda c: orig(c) * 0.5)
+    assert _fails([t8.test_decode_exhaustive_matches_torch, t8.test_format_facts], golden_dir)
+
+
+@pytest.mark.parametrize("mutant", [_ties_to_higher, _strict_past])
+def test_topk_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(od, "topk_select_row", mutant)
+    assert _fails(TOPK_PINS, golden_dir)
+
+
+@pytest.mark.parametrize("mutant", [_value_from_tail, _no_scale, _drop_duplicates])
+def test_attention_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(od, "sparse_mqa_attention_row", mutant)
+    assert _fails(ATTN_PINS, golden_dir)
