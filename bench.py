@@ -1,0 +1,234 @@
+"""Throughput of the DSA hot path (lightning indexer -> top-k -> sparse MQA
+attention) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_128k]
+
+A step is one dsa_forward call over one batch of seeded synthetic inputs that
+are already resident in HBM.  The default workload is decode at 128K context:
+64 sequences, each one new query token against a 131072-token cache (FP8
+indexer keys [131072,128] and bf16 latent KV [131072,576] per sequence,
+8 indexer heads, k = 2048, 128 query heads, value dim 512).  Prints one JSON
+line; ``value`` is query tokens per second.  The line also carries the
+roofline position of the step's dominant kernel (timed with HIP events on
+the stream it runs on) and the CPU oracle's throughput on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import long_context_02_amd as dsa  # noqa: E402
+from long_context_02_amd.synth import WORKLOADS, make_inputs  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one step (what the method must do, not what it skips)
+def work(wl):
+    t = np.arange(wl.T, dtype=np.int64)
+    n_cand = np.minimum(wl.N, wl.q_offset + t + 1)
+    n_sel = np.minimum(wl.k, n_cand)
+    idx_pairs = int(n_cand.sum()) * wl.B
+    attn_pairs = int(n_sel.sum()) * wl.B
+    keys_read = min(wl.N, wl.q_offset + wl.T) * wl.B
+    fp8 = wl.dtype == "bf16"
+    key_bytes = wl.d_I + 4 if fp8 else 4 * wl.d_I
+    qrow_bytes = wl.H_I * (wl.d_I + 8) if fp8 else wl.H_I * (4 * wl.d_I + 4)
+    el = 2 if fp8 else 4
+    kv_row = wl.d_qk * el
+    return {
+        "indexer": {
+            "flops": idx_pairs * 2 * wl.H_I * wl.d_I,
+            "bytes": keys_read * key_bytes + wl.B * wl.T * qrow_bytes,
+            "flop_unit": "fp8" if fp8 else "f32",
+        },
+        "topk": {"flops": 0, "bytes": idx_pairs * 4 + wl.B * wl.T * wl.k * 4, "flop_unit": None},
+        "attention": {
+            "flops": attn_pairs * 2 * wl.H * (wl.d_qk + wl.d_v),
+            # each selected latent row gathered once per query token, plus Q in and O out
+            "bytes": attn_pairs * kv_row + wl.B * wl.T * wl.H * (wl.d_qk + wl.d_v) * el,
+            "flop_unit": "bf16" if fp8 else "f32",
+        },
+    }
+
+
+def roofline(phase, w, seconds):
+    """Roofline position of one kernel: which roof binds, and the achieved rate."""
+    peak_f = {"fp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_TFLOPS}.get(w["flop_unit"])
+    t_mem = w["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_cmp = w["flops"] / (peak_f * 1e12) if peak_f else 0.0
+    if t_cmp > t_mem:
+        ach = w["flops"] / seconds / 1e12
+        return {"kernel": phase, "bound": "mfma", "achieved": round(ach, 2), "peak": peak_f,
+                "unit": "TFLOP/s", "frac": round(ach / peak_f, 4), "algorithmic": w["flops"]}
+    ach = w["bytes"] / seconds / 1e9
+    return {"kernel": phase, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic": w["bytes"]}
+
+
+# ---------------------------------------------------------------------------
+def timed(fn, steps, stream):
+    """Average milliseconds of fn() over `steps` launches, HIP events on `stream`."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(wl, g, budget_s):
+    """The CPU oracle on a bounded sample of the same workload: whole rows
+    (index scores -> selection -> attention), timed on this host's cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    fp8 = wl.dtype == "bf16"
+    rng = np.random.default_rng(0)
+    if wl.T == 1:
+        order = [(int(b), 0) for b in rng.permutation(wl.B)]
+    else:
+        order = [(0, int(t)) for t in rng.permutation(wl.T)]
+    done, spent = 0, 0.0
+    host = {}
+    for (b, t) in order:
+        if b not in host:  # host copies of this sequence (not timed)
+            host = {b: {
+                "k": g["k_idx"][b].cpu().numpy() if fp8 else g["k_idx"][b].double().cpu().numpy(),
+                "ks": g["k_idx_scale"][b].double().cpu().numpy() if fp8 else None,
+                "kv": g["kv"][b].float().cpu().numpy(),
+            }}
+        h = host[b]
+        qi = g["q_idx"][b, t].cpu().numpy() if fp8 else g["q_idx"][b, t].double().cpu().numpy()
+        qs = g["q_idx_scale"][b, t].double().cpu().numpy() if fp8 else None
+        w = g["w"][b, t].double().cpu().numpy()
+        q = g["q"][b, t].double().cpu().numpy()
+        t0 = time.perf_counter()
+        K = oracle.dequantize(h["k"], h["ks"]) if fp8 else h["k"]
+        qrow = oracle.dequantize(qi, qs) if fp8 else qi
+        n_cand = min(wl.N, wl.q_offset + t + 1)
+        I = oracle.index_scores_row(qrow, w, K, n_cand)
+        sel = oracle.topk_select_row(I, wl.k, n_cand)
+        oracle.sparse_mqa_attention_row(q, h["kv"], sel, wl.d_v, wl.sm_scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done / spent, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} query tokens of {wl.name} (whole rows: index scores, top-{wl.k}, "
+                      f"attention; float64), {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {wl.name} inputs on {dev}")
+    g = make_inputs(wl, seed=0, device=dev)
+    B, T, N = wl.B, wl.T, wl.N
+    out = torch.empty(B, T, wl.H, wl.d_v, dtype=g["q"].dtype, device=dev)
+    ws = torch.empty(dsa.workspace_size(dsa.OP_FORWARD, B, T, N, wl.H, wl.d_v, wl.k),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        dsa.forward(g["q_idx"], g["k_idx"], g["w"], g["q"], g["kv"], k=wl.k, q_offset=wl.q_offset,
+                    d_v=wl.d_v, sm_scale=wl.sm_scale, q_idx_scale=g["q_idx_scale"],
+                    k_idx_scale=g["k_idx_scale"], out=out, workspace=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ms = timed(step, args.steps, stream)
+
+    # the three kernels of a step, each timed on its own over the same number of launches
+    scores = torch.empty(B, T, N, dtype=torch.float32, device=dev)
+    idx = torch.empty(B, T, wl.k, dtype=torch.int32, device=dev)
+    attn_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_ATTN, B, T, N, wl.H, wl.d_v, wl.k)),
+                          dtype=torch.uint8, device=dev)
+    phases = {
+        "indexer": lambda: dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
+                                              q_idx_scale=g["q_idx_scale"],
+                                              k_idx_scale=g["k_idx_scale"], out=scores),
+        "topk": lambda: dsa.topk_select(scores, wl.k, wl.q_offset, out=idx),
+        "attention": lambda: dsa.sparse_mla_attn(g["q"], g["kv"], idx, wl.d_v, wl.sm_scale,
+                                                 out=out, lse=False, workspace=attn_ws),
+    }
+    phase_ms = {}
+    for name, fn in phases.items():
+        fn()
+        phase_ms[name] = timed(fn, args.steps, stream)
+    w = work(wl)
+    dom = max(phase_ms, key=phase_ms.get)
+    roof = roofline(dom, w[dom], phase_ms[dom] / 1e3)
+    roof["traffic"] = None
+
+    line = {
+        "metric": "DSA tokens/s (indexer+top-k+sparse attn) at 128K ctx; % of MFMA / HBM roofline",
+        "value": round(B * T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 indexer / bf16 attention" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded)",
+        "config": {"workload": wl.name, "batch": B, "query_tokens": T, "context": N,
+                   "q_offset": wl.q_offset, "indexer_heads": wl.H_I, "indexer_dim": wl.d_I,
+                   "top_k": wl.k, "heads": wl.H, "d_qk": wl.d_qk, "d_v": wl.d_v,
+                   "parallelism": "single GPU"},
+        "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        line["cpu_baseline"] = cpu_baseline(wl, g, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) hot path of DeepSeek Sparse
+ * Attention (DSA): lightning-indexer scores, per-query top-k token selection,
+ * and sparse MLA attention in MQA mode.
+ *
+ * Source of the method: "Paper Breakdown: DeepSeek-V3.2", section 2
+ * "Architecture: DSA (§2.1)" (index-score formula, top-k selector, attention
+ * over the selected latent entries, "DSA under MLA (MQA Mode)"), and
+ * "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models", Key
+ * points (k = 2048 selected tokens, ReLU, few indexer heads, FP8, MLA in MQA
+ * mode).
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor argument is a DEVICE pointer to contiguous row-major memory
+ *    (last dimension innermost) that the CALLER owns.  Pointers must be
+ *    16-byte aligned.  The library never allocates, frees or synchronises
+ *    device memory; kernels are enqueued on `stream` (a hipStream_t, NULL =
+ *    the default stream) and the call returns without waiting.
+ *  - Query token t of batch entry b sits at absolute position q_offset + t
+ *    and its causal candidate set is s in [0, min(N, q_offset + t + 1)).
+ *    Prefill: T = N, q_offset = 0.  Decode: T = 1, q_offset = N - 1.
+ *    Chunked prefill: q_offset = N - T.
+ *  - Arguments are checked on the host before anything is launched; a bad
+ *    argument returns DSA_ERR_INVALID_ARG, a shape outside the supported set
+ *    returns DSA_ERR_UNSUPPORTED, a too-small workspace DSA_ERR_WORKSPACE and
+ *    a failed launch DSA_ERR_HIP.  No exception crosses the ABI.  Device data
+ *    is never validated (NaN inputs do not fault; see each call).
+ *  - Stateless and re-entrant: concurrent calls on different streams with
+ *    disjoint outputs and workspaces are safe.
+ *
+ * Supported shapes
+ *  - indexer: (H_I, d_I, idx_dtype) = (8, 128, DSA_FP8_E4M3FN) or
+ *    (1..16, 1..256, DSA_F32);
+ *  - attention: (H, d_qk, d_v, attn_dtype) = (128, 576, 512, DSA_BF16) or
+ *    (1..32, 1..256, 1..d_qk, DSA_F32);
+ *  - 1 <= k <= 2048; q_offset >= 0; q_offset + T <= N; B*T*N < 2^40.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define DSA_API __attribute__((visibility("default")))
+#else
+#define DSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,
+    DSA_ERR_UNSUPPORTED = 2,
+    DSA_ERR_WORKSPACE = 3,
+    DSA_ERR_BAD_INDEX = 4,
+    DSA_ERR_HIP = 5
+} dsa_status;
+
+typedef enum dsa_dtype {
+    DSA_F32 = 0,        /* IEEE binary32 */
+    DSA_BF16 = 1,       /* bfloat16 */
+    DSA_FP8_E4M3FN = 2  /* OCP 8-bit float E4M3 (bias 7, max 448, 0x7F/0xFF NaN) */
+} dsa_dtype;
+
+typedef enum dsa_op {
+    DSA_OP_TOPK = 0,
+    DSA_OP_ATTN = 1,
+    DSA_OP_FORWARD = 2
+} dsa_op;
+
+/*
+ * Lightning-indexer scores ("Paper Breakdown: DeepSeek-V3.2", section 2,
+ * index-score formula):
+ *     scores[b,t,s] = sum_j w[b,t,j] * ReLU(q_idx[b,t,j,:] . k_idx[b,s,:])
+ * for s <= q_offset + t, and -inf for every other s < N.  One indexer key per
+ * token is shared by all H_I heads.
+ *
+ *  q_idx       [B,T,H_I,d_I]  FP8 codes (uint8) or f32, per idx_dtype
+ *  q_idx_scale [B,T,H_I] f32  dequantisation scale of each query head
+ *                             (FP8 only; must be NULL for f32)
+ *  k_idx       [B,N,d_I]      FP8 codes or f32
+ *  k_idx_scale [B,N]     f32  dequantisation scale of each key (FP8 only)
+ *  w           [B,T,H_I] f32  head weights w[t,j] (any sign)
+ *  scores      [B,T,N]   f32  output, fully overwritten
+ * With FP8 the value of an operand is scale * decode(code); the kernel
+ * computes k_scale * sum_j (w * q_scale) * ReLU(q8 . k8) with an exact FP8
+ * product and fp32 accumulation, which equals the formula for positive
+ * scales (the only kind the amax/448 rule produces).  Accumulation is fp32.
+ */
+DSA_API dsa_status dsa_indexer_scores(const void* q_idx, const float* q_idx_scale,
+                              const void* k_idx, const float* k_idx_scale,
+                              const float* w, float* scores,
+                              int B, int T, int N, int H_I, int d_I, int q_offset,
+                              dsa_dtype idx_dtype, void* stream);
+
+/*
+ * Top-k token selection ("Paper Breakdown: DeepSeek-V3.2", section 2: query t
+ * keeps the tokens whose score is in Top-k(I[t,:]); the selector keeps only
+ * earlier tokens, "DeepSeek V3.2: Sparse Attention and Reinforcement Learning
+ * Updates", Summary).
+ *
+ *  scores [B,T,N] f32   only s < min(N, q_offset+t+1) is read per row
+ *  idx    [B,T,k] int32 output: the n = min(k, #candidates) selected token
+ *                       indices in ascending order, then -1 padding
+ * Ranking: larger score first; equal scores go to the lower index; -0 equals
+ * +0; NaN ranks below every number.  The result is unique and deterministic.
+ * workspace may be NULL when dsa_workspace_size(DSA_OP_TOPK, ...) is 0.
+ */
+DSA_API dsa_status dsa_topk_select(const float* scores, int32_t* idx,
+                           int B, int T, int N, int k, int q_offset,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse MLA attention in MQA mode ("Paper Breakdown: DeepSeek-V3.2",
+ * section 2, attention formula u_t = Attn(h_t, {c_s : selected}) and "DSA
+ * under MLA (MQA Mode)": every query head attends to the same latent vector
+ * c_s of each selected token):
+ *     z[h,i]   = sm_scale * q[b,t,h,:] . kv[b,idx[b,t,i],:]        (d_qk wide)
+ *     out[b,t,h,:] = sum_i softmax_i(z[h,:]) * kv[b,idx[b,t,i],0:d_v]
+ *     lse[b,t,h]   = log sum_i exp(z[h,i])
+ *
+ *  q   [B,T,H,d_qk] bf16 or f32 (attn_dtype)
+ *  kv  [B,N,d_qk]   bf16 or f32: latent (first d_v columns, also the value)
+ *                   followed by the rope part
+ *  idx [B,T,k] int32: slots equal to -1 or otherwise outside [0, N) are
+ *                   skipped; duplicates count once per occurrence
+ *  out [B,T,H,d_v]  bf16 or f32 (attn_dtype), fully overwritten
+ *  lse [B,T,H] f32 or NULL
+ * A row with no valid slot gets out = 0 and lse = -inf.  bf16 runs the
+ * products on bf16 MFMA with fp32 logits/softmax/accumulation and rounds the
+ * softmax weights to bf16 before the value product.
+ */
+DSA_API dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx,
+                               void* out, float* lse,
+                               int B, int T, int N, int H, int d_qk, int d_v, int k,
+                               float sm_scale, dsa_dtype attn_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole DSA path: indexer scores -> top-k selection -> sparse attention,
+ * for prefill, decode and chunked prefill alike (see q_offset above).
+ * Arguments are those of the three calls above; idx_out [B,T,k] receives the
+ * selected indices when non-NULL.  The workspace holds the score matrix and
+ * the other intermediates: size it with dsa_workspace_size(DSA_OP_FORWARD).
+ */
+DSA_API dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale,
+                       const void* k_idx, const float* k_idx_scale,
+                       const float* w, const void* q, const void* kv,
+                       void* out, float* lse, int32_t* idx_out,
+                       int B, int T, int N, int H_I, int d_I, int H, int d_qk, int d_v,
+                       int k, int q_offset, float sm_scale,
+                       dsa_dtype idx_dtype, dsa_dtype attn_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by op (a dsa_op) for these sizes; 0 means none.
+ * Returns (size_t)-1 for arguments that no call would accept.
+ */
+DSA_API size_t dsa_workspace_size(int op, int B, int T, int N, int H, int d_v, int k);
+
+/* Static, NUL-terminated description of a status code. */
+DSA_API const char* dsa_status_string(dsa_status s);
+
+/* ABI version: (major << 16) | minor. */
+DSA_API int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,201 @@
+// C ABI of libdsa: argument checks, workspace carving and kernel launches.
+// Every entry point checks its arguments on the host before launching
+// anything, never allocates, frees or synchronises, and reports launch
+// failures as DSA_ERR_HIP.
+#include <cmath>
+#include <cstdint>
+
+#include "dsa_internal.h"
+
+using namespace dsa;
+
+namespace {
+
+constexpr int kMaxK = 2048;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dsa_status check_common(int B, int T, int N, int q_offset) {
+    if (B < 1 || T < 1 || N < 1 || q_offset < 0) return DSA_ERR_INVALID_ARG;
+    if ((long long)q_offset + T > N) return DSA_ERR_INVALID_ARG;
+    if ((long long)B * T * (long long)N >= (1LL << 40)) return DSA_ERR_UNSUPPORTED;
+    if (B > 65535) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
+dsa_status check_indexer(const void* q_idx, const float* q_scale, const void* k_idx,
+                         const float* k_scale, const float* w, const float* scores, int B, int T,
+                         int N, int H_I, int d_I, int q_offset, dsa_dtype dt) {
+    if (!q_idx || !k_idx || !w || !scores) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w) || !aligned16(scores))
+        return DSA_ERR_INVALID_ARG;
+    dsa_status st = check_common(B, T, N, q_offset);
+    if (st != DSA_OK) return st;
+    if (dt == DSA_FP8_E4M3FN) {
+        if (!q_scale || !k_scale || !aligned16(q_scale) || !aligned16(k_scale))
+            return DSA_ERR_INVALID_ARG;
+        if (H_I != 8 || d_I != 128) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    }
+    if (dt == DSA_F32) {
+        if (q_scale || k_scale) return DSA_ERR_INVALID_ARG;
+        if (H_I < 1 || H_I > 16 || d_I < 1 || d_I > 256 || H_I * d_I > 4096) return DSA_ERR_UNSUPPORTED;
+        if (T > 65535) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    }
+    return dt == DSA_BF16 ? DSA_ERR_UNSUPPORTED : DSA_ERR_INVALID_ARG;
+}
+
+dsa_status check_attn(const void* q, const void* kv, const int32_t* idx, const void* out,
+                      const float* lse, int B, int T, int N, int H, int d_qk, int d_v, int k,
+                      float sm_scale, dsa_dtype dt) {
+    if (!q || !kv || !idx || !out) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(idx) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return DSA_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || N < 1 || k < 1) return DSA_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale)) return DSA_ERR_INVALID_ARG;
+    if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+    if (B > 65535 || T > 65535) return DSA_ERR_UNSUPPORTED;
+    if ((long long)B * N * (long long)(d_qk > 0 ? d_qk : 1) >= (1LL << 42)) return DSA_ERR_UNSUPPORTED;
+    if (dt == DSA_BF16) {
+        if (H != 128 || d_qk != 576 || d_v != 512) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    }
+    if (dt == DSA_F32) {
+        if (H < 1 || H > 32 || d_qk < 1 || d_qk > 256 || d_v < 1 || d_v > d_qk) return DSA_ERR_UNSUPPORTED;
+        return DSA_OK;
+    }
+    return dt == DSA_FP8_E4M3FN ? DSA_ERR_UNSUPPORTED : DSA_ERR_INVALID_ARG;
+}
+
+size_t attn_ws(int B, int T, int H, int d_v, int k) {
+    const dsa_dtype dt = (H == 128 && d_v == 512) ? DSA_BF16 : DSA_F32;
+    return attn_workspace_bytes(B, T, H, d_v, k, dt);
+}
+
+dsa_status run_indexer(const void* q_idx, const float* q_scale, const void* k_idx,
+                       const float* k_scale, const float* w, float* scores, int B, int T, int N,
+                       int H_I, int d_I, int q_offset, dsa_dtype dt, bool fill, hipStream_t s) {
+    if (dt == DSA_FP8_E4M3FN)
+        return launch_indexer_fp8(static_cast<const uint8_t*>(q_idx), q_scale,
+                                  static_cast<const uint8_t*>(k_idx), k_scale, w, scores, B, T, N,
+                                  q_offset, fill, s);
+    return launch_indexer_f32(static_cast<const float*>(q_idx), static_cast<const float*>(k_idx),
+                              w, scores, B, T, N, H_I, d_I, q_offset, fill, s);
+}
+
+dsa_status run_attn(const void* q, const void* kv, const int32_t* idx, void* out, float* lse,
+                    int B, int T, int N, int H, int d_qk, int d_v, int k, float sm_scale,
+                    dsa_dtype dt, void* ws, hipStream_t s) {
+    if (dt == DSA_BF16) return launch_attn_bf16(q, kv, idx, out, lse, B, T, N, k, sm_scale, ws, s);
+    return launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(kv), idx,
+                           static_cast<float*>(out), lse, B, T, N, H, d_qk, d_v, k, sm_scale, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return (1 << 16) | 0; }
+
+const char* dsa_status_string(dsa_status s) {
+    switch (s) {
+        case DSA_OK: return "DSA_OK: success";
+        case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape or dtype not supported";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace too small";
+        case DSA_ERR_BAD_INDEX: return "DSA_ERR_BAD_INDEX: index out of range";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP launch failed";
+    }
+    return "unknown dsa_status";
+}
+
+size_t dsa_workspace_size(int op, int B, int T, int N, int H, int d_v, int k) {
+    if (B < 1 || T < 1 || N < 1 || k < 1 || k > kMaxK || H < 1 || d_v < 1) return (size_t)-1;
+    switch (op) {
+        case DSA_OP_TOPK: return topk_workspace_bytes(B, T, N, k);
+        case DSA_OP_ATTN: return attn_ws(B, T, H, d_v, k);
+        case DSA_OP_FORWARD:
+            return align_up((size_t)B * T * N * sizeof(float)) +
+                   align_up((size_t)B * T * k * sizeof(int32_t)) +
+                   align_up(topk_workspace_bytes(B, T, N, k)) + attn_ws(B, T, H, d_v, k);
+        default: return (size_t)-1;
+    }
+}
+
+dsa_status dsa_indexer_scores(const void* q_idx, const float* q_idx_scale, const void* k_idx,
+                              const float* k_idx_scale, const float* w, float* scores, int B,
+                              int T, int N, int H_I, int d_I, int q_offset, dsa_dtype idx_dtype,
+                              void* stream) {
+    dsa_status st = check_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w, scores, B, T, N, H_I,
+                                  d_I, q_offset, idx_dtype);
+    if (st != DSA_OK) return st;
+    return run_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w, scores, B, T, N, H_I, d_I,
+                       q_offset, idx_dtype, true, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_topk_select(const float* scores, int32_t* idx, int B, int T, int N, int k,
+                           int q_offset, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!scores || !idx || !aligned16(scores) || !aligned16(idx)) return DSA_ERR_INVALID_ARG;
+    dsa_status st = check_common(B, T, N, q_offset);
+    if (st != DSA_OK) return st;
+    if (k < 1) return DSA_ERR_INVALID_ARG;
+    if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+    const size_t need = topk_workspace_bytes(B, T, N, k);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    return launch_topk(scores, idx, B, T, N, k, q_offset, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx, void* out,
+                               float* lse, int B, int T, int N, int H, int d_qk, int d_v, int k,
+                               float sm_scale, dsa_dtype attn_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    dsa_status st = check_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype);
+    if (st != DSA_OK) return st;
+    const size_t need = attn_workspace_bytes(B, T, H, d_v, k, attn_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return DSA_ERR_WORKSPACE;
+    return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* k_idx,
+                       const float* k_idx_scale, const float* w, const void* q, const void* kv,
+                       void* out, float* lse, int32_t* idx_out, int B, int T, int N, int H_I,
+                       int d_I, int H, int d_qk, int d_v, int k, int q_offset, float sm_scale,
+                       dsa_dtype idx_dtype, dsa_dtype attn_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    // the indexer's output goes to the workspace, so pass a stand-in for the check
+    dsa_status st = check_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w,
+                                  reinterpret_cast<const float*>(16), B, T, N, H_I, d_I, q_offset,
+                                  idx_dtype);
+    if (st != DSA_OK) return st;
+    st = check_attn(q, kv, reinterpret_cast<const int32_t*>(16), out, lse, B, T, N, H, d_qk, d_v, k,
+                    sm_scale, attn_dtype);
+    if (st != DSA_OK) return st;
+    if (idx_out && !aligned16(idx_out)) return DSA_ERR_INVALID_ARG;
+    const size_t need = dsa_workspace_size(DSA_OP_FORWARD, B, T, N, H, d_v, k);
+    if (need == (size_t)-1) return DSA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
+
+    char* p = static_cast<char*>(workspace);
+    float* scores = reinterpret_cast<float*>(p);
+    p += align_up((size_t)B * T * N * sizeof(float));
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)B * T * k * sizeof(int32_t));
+    void* topk_ws = p;
+    p += align_up(topk_workspace_bytes(B, T, N, k));
+    void* attn_w = p;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w, scores, B, T, N, H_I, d_I, q_offset,
+                     idx_dtype, false, s);
+    if (st != DSA_OK) return st;
+    st = launch_topk(scores, idx, B, T, N, k, q_offset, topk_ws, s);
+    if (st != DSA_OK) return st;
+    return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, attn_w, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,324 @@
+// Lightning-indexer scores on gfx950.
+//
+// Formula ("Paper Breakdown: DeepSeek-V3.2", section 2 "Architecture: DSA
+// (§2.1)"): I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]), one key per token
+// shared by the H_I = 8 indexer heads, FP8 operands.
+//
+// FP8 path.  The contraction over d_I = 128 is exactly one
+// v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3 -> fp32).  The 16 MFMA rows are
+// (4 queries x 4 heads); two MFMAs (heads 0-3 and 4-7) put all 8 head dots
+// of one (query, key) pair in the same lane, so ReLU, the (w * q_scale)
+// weighted head sum and the key scale run in registers with no cross-lane
+// traffic, and each lane stores one finished fp32 score.
+//
+//  * indexer_fp8_tiled  (T >= 16): a workgroup owns 64 queries (16 per wave)
+//    and a range of keys; 64-key tiles are staged through LDS (rows padded
+//    to 144 B so the 16 lanes that read one 32-byte slice of 16 different
+//    keys hit distinct banks) and double-buffered: the next tile's global
+//    loads are in flight while the current tile is multiplied.
+//  * indexer_fp8_stream (T < 16, e.g. decode): the key stream is read once,
+//    so each wave loads its 16-key fragments straight from HBM, four
+//    fragments in flight per wave.
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int HI = 8;      // indexer heads
+constexpr int DI = 128;    // indexer dim = bytes per FP8 row
+constexpr int NT = 256;    // threads per workgroup (4 waves)
+
+// C[16x16] = A[16x128] * B[128x16], FP8 e4m3 both sides, fp32 result.
+// A lane l holds row l%16, B lane l holds column l%16, each as 32 bytes of
+// the 128-byte vector starting at byte 32*(l/16); A and B use the same byte
+// slice, so every q byte meets the matching k byte.  C lane l holds rows
+// 4*(l/16)+i (i = 0..3) of column l%16.
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 pack8(const uint4& x0, const uint4& x1) {
+    return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                 (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
+// sum_j ws[j] * ReLU(D_j): acc0 holds heads 0-3, acc1 heads 4-7.
+__device__ __forceinline__ float head_sum(const f32x4& acc0, const f32x4& acc1, const float* ws) {
+    float s = ws[0] * fmaxf(acc0[0], 0.f);
+    s = fmaf(ws[1], fmaxf(acc0[1], 0.f), s);
+    s = fmaf(ws[2], fmaxf(acc0[2], 0.f), s);
+    s = fmaf(ws[3], fmaxf(acc0[3], 0.f), s);
+    s = fmaf(ws[4], fmaxf(acc1[0], 0.f), s);
+    s = fmaf(ws[5], fmaxf(acc1[1], 0.f), s);
+    s = fmaf(ws[6], fmaxf(acc1[2], 0.f), s);
+    s = fmaf(ws[7], fmaxf(acc1[3], 0.f), s);
+    return s;
+}
+
+// Load the A fragments (one query group of 4 queries, both head halves) and
+// the per-lane head weights w * q_scale of the query whose scores this lane
+// produces.  Queries at or beyond T get zeros.
+__device__ __forceinline__ void load_queries(const uint8_t* __restrict__ q,
+                                             const float* __restrict__ qs,
+                                             const float* __restrict__ w, size_t row0,
+                                             int tq0, int T, int lane, i32x8* a, float* ws) {
+    const int m = lane & 15, kb = lane >> 4;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int t = tq0 + (m >> 2), h = 4 * hh + (m & 3);
+        if (t < T) {
+            const uint4* p = reinterpret_cast<const uint4*>(q + ((row0 + t) * HI + h) * DI + 32 * kb);
+            a[hh] = pack8(p[0], p[1]);
+        } else {
+            a[hh] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    const int t = tq0 + kb;
+#pragma unroll
+    for (int j = 0; j < HI; ++j)
+        ws[j] = t < T ? w[(row0 + t) * HI + j] * qs[(row0 + t) * HI + j] : 0.f;
+}
+
+__device__ void fill_neg_inf(float* __restrict__ out_b, int t0, int t1, int N, int s0, int s1) {
+    const float ninf = -__builtin_inff();
+    for (int t = t0; t < t1; ++t)
+        for (int s = s0 + (int)threadIdx.x; s < s1; s += NT) out_b[(size_t)t * N + s] = ninf;
+}
+
+// ---------------------------------------------------------------------------
+constexpr int TQB = 64;     // queries per workgroup (tiled)
+constexpr int TILE = 64;    // keys per LDS tile
+constexpr int ROWB = 144;   // LDS bytes per key row (128 + 16 pad)
+
+template <bool FILL>
+__global__ __launch_bounds__(NT) void indexer_fp8_tiled(
+    const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
+    const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
+    int T, int N, int q_offset, int keys_per_wg) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TILE * ROWB];
+    __shared__ float lds_ks[2][TILE];
+
+    const int b = blockIdx.z;
+    const int t0 = blockIdx.x * TQB;
+    const int s_begin = blockIdx.y * keys_per_wg;
+    const int s_end = min(N, s_begin + keys_per_wg);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, kb = lane >> 4;
+    const int t_end = min(T, t0 + TQB);
+    const int s_vis = min(s_end, q_offset + t_end);  // keys [s_begin, s_vis) are visible to some query
+    const size_t row0 = (size_t)b * T;
+    float* __restrict__ out_b = scores + row0 * N;
+    const uint8_t* __restrict__ k_b = k + (size_t)b * N * DI;
+    const float* __restrict__ ks_b = ks + (size_t)b * N;
+
+    const int n_tiles = s_vis > s_begin ? (s_vis - s_begin + TILE - 1) / TILE : 0;
+    if (n_tiles > 0) {
+        const int tw0 = t0 + 16 * wave;
+        i32x8 a[4][2];
+        float ws[4][HI];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) load_queries(q, qs, w, row0, tw0 + 4 * g, T, lane, a[g], ws[g]);
+
+        // cooperative staging: 512 16-byte chunks per tile, two per thread
+        const int c_key0 = tid >> 3, c_key1 = (tid + NT) >> 3, c_piece = tid & 7;
+        uint4 r0, r1;
+        float rks = 0.f;
+        auto fetch = [&](int s0) {
+            const uint4 zero = {0u, 0u, 0u, 0u};
+            const int s_a = s0 + c_key0, s_b = s0 + c_key1;
+            r0 = s_a < N ? *reinterpret_cast<const uint4*>(k_b + (size_t)s_a * DI + 16 * c_piece) : zero;
+            r1 = s_b < N ? *reinterpret_cast<const uint4*>(k_b + (size_t)s_b * DI + 16 * c_piece) : zero;
+            if (tid < TILE) rks = (s0 + tid) < N ? ks_b[s0 + tid] : 0.f;
+        };
+        auto stage = [&](int buf) {
+            *reinterpret_cast<uint4*>(&lds_k[buf][c_key0 * ROWB + 16 * c_piece]) = r0;
+            *reinterpret_cast<uint4*>(&lds_k[buf][c_key1 * ROWB + 16 * c_piece]) = r1;
+            if (tid < TILE) lds_ks[buf][tid] = rks;
+        };
+
+        fetch(s_begin);
+        stage(0);
+        __syncthreads();
+        for (int it = 0; it < n_tiles; ++it) {
+            const int s0 = s_begin + it * TILE;
+            const int buf = it & 1;
+            const bool more = it + 1 < n_tiles;
+            if (more) fetch(s0 + TILE);
+            if (tw0 < t_end) {
+#pragma unroll
+                for (int sub = 0; sub < TILE / 16; ++sub) {
+                    const int key = 16 * sub + m;
+                    const uint8_t* src = &lds_k[buf][key * ROWB + 32 * kb];
+                    const i32x8 bf = pack8(*reinterpret_cast<const uint4*>(src),
+                                           *reinterpret_cast<const uint4*>(src + 16));
+                    const float ksc = lds_ks[buf][key];
+                    const int s_abs = s0 + key;
+                    f32x4 acc[4][2];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        acc[g][0] = mfma_fp8(a[g][0], bf);
+                        acc[g][1] = mfma_fp8(a[g][1], bf);
+                    }
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int t = tw0 + 4 * g + kb;
+                        float sc = head_sum(acc[g][0], acc[g][1], ws[g]) * ksc;
+                        if (s_abs > q_offset + t) sc = -__builtin_inff();
+                        if (t < T && s_abs < s_end) out_b[(size_t)t * N + s_abs] = sc;
+                    }
+                }
+            }
+            if (more) stage(buf ^ 1);
+            __syncthreads();
+        }
+    }
+    if (FILL) {
+        const int f0 = s_begin + n_tiles * TILE;
+        if (f0 < s_end) fill_neg_inf(out_b, t0, t_end, N, f0, s_end);
+    }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int SQ = 4;      // queries per workgroup (stream)
+constexpr int SU = 4;      // 16-key fragments in flight per wave
+
+template <bool FILL>
+__global__ __launch_bounds__(NT) void indexer_fp8_stream(
+    const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
+    const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
+    int T, int N, int q_offset, int keys_per_wg) {
+    const int b = blockIdx.z;
+    const int tq0 = blockIdx.y * SQ;
+    const int s_begin = blockIdx.x * keys_per_wg;
+    const int s_end = min(N, s_begin + keys_per_wg);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, kb = lane >> 4;
+    const int t_end = min(T, tq0 + SQ);
+    const int s_vis = min(s_end, q_offset + t_end);
+    const size_t row0 = (size_t)b * T;
+    float* __restrict__ out_b = scores + row0 * N;
+    const uint8_t* __restrict__ k_b = k + (size_t)b * N * DI;
+    const float* __restrict__ ks_b = ks + (size_t)b * N;
+
+    i32x8 a[2];
+    float ws[HI];
+    load_queries(q, qs, w, row0, tq0, T, lane, a, ws);
+    const int t = tq0 + kb;
+
+    // wave w reads fragments w, w+4, w+8, ... of the workgroup's key range, so
+    // one round of the four waves covers 64*SU consecutive keys
+    for (int base = s_begin + 16 * wave; base < s_vis; base += 64 * SU) {
+        uint4 x0[SU], x1[SU];
+        float kss[SU];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int s = base + 64 * u + m;
+            if (s < s_vis) {
+                const uint4* p = reinterpret_cast<const uint4*>(k_b + (size_t)s * DI + 32 * kb);
+                x0[u] = p[0];
+                x1[u] = p[1];
+                kss[u] = ks_b[s];
+            } else {
+                x0[u] = x1[u] = uint4{0u, 0u, 0u, 0u};
+                kss[u] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int s0 = base + 64 * u;
+            if (s0 < s_vis) {
+                const i32x8 bf = pack8(x0[u], x1[u]);
+                const f32x4 acc0 = mfma_fp8(a[0], bf);
+                const f32x4 acc1 = mfma_fp8(a[1], bf);
+                const int s_abs = s0 + m;
+                float sc = head_sum(acc0, acc1, ws) * kss[u];
+                if (s_abs > q_offset + t) sc = -__builtin_inff();
+                if (t < t_end && s_abs < s_end) out_b[(size_t)t * N + s_abs] = sc;
+            }
+        }
+    }
+    if (FILL) {
+        // fragments cover [s_begin, s_vis) rounded up to 16; fill the rest
+        const int f0 = s_begin + ((max(s_vis - s_begin, 0) + 15) / 16) * 16;
+        if (f0 < s_end) fill_neg_inf(out_b, tq0, t_end, N, f0, s_end);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 reference-precision path (small head counts and dims): one thread per
+// (query, key), the query row in LDS.
+constexpr int F32_MAX_HD = 4096;
+
+__global__ __launch_bounds__(NT) void indexer_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ w,
+    float* __restrict__ scores, int T, int N, int H_I, int d_I, int q_offset, int fill) {
+    __shared__ float qrow[F32_MAX_HD];
+    __shared__ float wrow[16];
+    const int b = blockIdx.z, t = blockIdx.y;
+    const size_t row = (size_t)b * T + t;
+    for (int i = threadIdx.x; i < H_I * d_I; i += NT) qrow[i] = q[row * H_I * d_I + i];
+    if (threadIdx.x < H_I) wrow[threadIdx.x] = w[row * H_I + threadIdx.x];
+    __syncthreads();
+    const int s = blockIdx.x * NT + threadIdx.x;
+    if (s >= N) return;
+    float* dst = scores + row * N + s;
+    if (s > q_offset + t) {
+        if (fill) *dst = -__builtin_inff();
+        return;
+    }
+    const float* kr = k + ((size_t)b * N + s) * d_I;
+    float acc = 0.f;
+    for (int j = 0; j < H_I; ++j) {
+        float dot = 0.f;
+        for (int d = 0; d < d_I; ++d) dot = fmaf(qrow[j * d_I + d], kr[d], dot);
+        acc = fmaf(wrow[j], fmaxf(dot, 0.f), acc);
+    }
+    *dst = acc;
+}
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* k,
+                              const float* ks, const float* w, float* scores,
+                              int B, int T, int N, int q_offset, bool fill_masked,
+                              hipStream_t stream) {
+    const long long n_vis = fill_masked ? N : std::min<long long>(N, (long long)q_offset + T);
+    if (T >= 16) {
+        const int nqb = ceil_div(T, TQB);
+        // aim for >= 2048 workgroups; key ranges are whole tiles, 256..8192 keys
+        long long kpw = (long long)nqb * B * n_vis / 2048;
+        kpw = std::max<long long>(256, std::min<long long>(8192, kpw));
+        kpw = (kpw + TILE - 1) / TILE * TILE;
+        dim3 grid(nqb, ceil_div(n_vis, kpw), B);
+        if (fill_masked)
+            indexer_fp8_tiled<true><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+        else
+            indexer_fp8_tiled<false><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+    } else {
+        const int nqg = ceil_div(T, SQ);
+        long long kpw = (long long)nqg * B * n_vis / 4096;
+        kpw = std::max<long long>(1024, std::min<long long>(16384, kpw));
+        kpw = (kpw + 64 * SU - 1) / (64 * SU) * (64 * SU);
+        dim3 grid(ceil_div(n_vis, kpw), nqg, B);
+        if (fill_masked)
+            indexer_fp8_stream<true><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+        else
+            indexer_fp8_stream<false><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+    }
+    return launch_status();
+}
+
+dsa_status launch_indexer_f32(const float* q, const float* k, const float* w, float* scores,
+                              int B, int T, int N, int H_I, int d_I, int q_offset,
+                              bool fill_masked, hipStream_t stream) {
+    if (H_I * d_I > F32_MAX_HD || H_I > 16) return DSA_ERR_UNSUPPORTED;
+    dim3 grid(ceil_div(N, NT), T, B);
+    indexer_f32_kernel<<<grid, NT, 0, stream>>>(q, k, w, scores, T, N, H_I, d_I, q_offset,
+                                                fill_masked ? 1 : 0);
+    return launch_status();
+}
+
+}  // namespace dsa

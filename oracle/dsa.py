@@ -182,7 +182,7 @@ def sparse_mqa_attention_row(q_row, kv, idx_row, d_v, sm_scale):
     H = q_row.shape[0]
     if sel.size == 0:
         return np.zeros((H, d_v)), np.full(H, -np.inf)
-    C = kv[sel]                                  # [k', d_qk]
+    C = np.asarray(kv[sel], dtype=np.float64)    # [k', d_qk], exact widening
     z = sm_scale * (q_row @ C.T)                 # [H, k'] logits
     m = z.max(axis=1, keepdims=True)
     p = np.exp(z - m)
@@ -208,13 +208,10 @@ def sparse_mqa_attention(q, kv, idx, d_v, sm_scale, rows=None):
         rows = [(b, t) for b in range(B) for t in range(T)]
     out = np.empty((len(rows), H, d_v))
     lse = np.empty((len(rows), H))
-    cache = {}
     for r, (b, t) in enumerate(rows):
-        if b not in cache:
-            cache = {b: kv[b].astype(np.float64)}
         irow = idx[b, t] if (full or idx.ndim == 3) else idx[r]
         out[r], lse[r] = sparse_mqa_attention_row(
-            q[b, t].astype(np.float64), cache[b], irow, d_v, sm_scale)
+            q[b, t].astype(np.float64), kv[b], irow, d_v, sm_scale)
     if full:
         return out.reshape(B, T, H, d_v), lse.reshape(B, T, H)
     return out, lse

@@ -1,0 +1,123 @@
+"""Shared helpers of the GPU parity tests: device handling, conversion of the
+synthetic inputs for the oracle, and the comparison rules.
+
+Comparison rules
+* index sets (selected tokens): the GPU row must hold n = min(k, #candidates)
+  distinct in-range indices in ascending order followed by -1; its symmetric
+  difference with the oracle's set may only contain tokens whose oracle score
+  lies within 1e-3 relative of the oracle's k-th largest score (when that
+  threshold is 0 the band is the exact zeros);
+* top-k on identical fp32 inputs: bit-exact;
+* attention outputs: the oracle recomputes attention on the GPU's own index
+  set; bf16 must be within 2e-2 max-abs and 5e-3 mean-abs, fp32 within 1e-5
+  max-abs;
+* index scores: |gpu - oracle| <= 1e-5 |oracle| + 1e-6 max|oracle row| (fp32
+  accumulation of exact FP8 products, then an 8-term fp32 weighted sum).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 5e-3
+F32_MAX_ABS = 1e-5
+BAND_REL = 1e-3
+
+
+def gpu_device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    return torch.device("cuda:0")
+
+
+def np64(t):
+    """Exact float64 copy of a CPU/GPU tensor (bf16/f32 widen exactly)."""
+    if t is None:
+        return None
+    if t.dtype == torch.uint8:
+        return t.detach().cpu().numpy()
+    return t.detach().cpu().double().numpy()
+
+
+def oracle_inputs(inp, b_sel=None):
+    """numpy views of the inputs for the oracle (optionally batch entries b_sel)."""
+    def pick(x):
+        if x is None:
+            return None
+        if b_sel is not None:
+            x = x[b_sel]
+        return np64(x)
+    return {k: pick(inp[k]) for k in ("q_idx", "q_idx_scale", "k_idx", "k_idx_scale", "w", "q", "kv")}
+
+
+def to_device(inp, dev):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def check_index_set(gpu_row, oracle_scores_row, oracle_sel, k, n_cand, where=""):
+    """Index-set rule; returns True when the set equals the oracle's exactly."""
+    g = np.asarray(gpu_row, dtype=np.int64)
+    n = min(k, n_cand)
+    sel = g[:n]
+    assert np.all(g[n:] == -1), f"{where}: padding is not -1"
+    assert np.all((sel >= 0) & (sel < n_cand)), f"{where}: index out of the causal range"
+    assert np.all(np.diff(sel) > 0), f"{where}: indices not strictly ascending"
+    o = np.asarray(oracle_sel, dtype=np.int64)[:n]
+    diff = np.setxor1d(sel, o)
+    if diff.size == 0:
+        return True
+    v = oracle_scores_row[:n_cand]
+    thr = np.partition(v, n_cand - n)[n_cand - n] if n_cand > k else -np.inf
+    dv = np.abs(oracle_scores_row[diff] - thr)
+    ok = dv <= BAND_REL * abs(thr) if thr != 0 else oracle_scores_row[diff] == 0
+    assert np.all(ok), (f"{where}: tokens {diff[~ok][:8]} differ from the oracle's selection with "
+                        f"scores {oracle_scores_row[diff[~ok][:8]]} vs threshold {thr}")
+    return False
+
+
+def check_scores(gpu, ref, where=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape
+    ninf_g, ninf_r = np.isneginf(gpu), np.isneginf(ref)
+    assert np.array_equal(ninf_g, ninf_r), f"{where}: -inf pattern differs"
+    fin = ~ninf_r
+    rowmax = np.max(np.where(fin, np.abs(ref), 0), axis=-1, keepdims=True)
+    tol = 1e-5 * np.abs(ref) + 1e-6 * rowmax
+    err = np.abs(np.where(fin, gpu - ref, 0))
+    bad = err > np.where(fin, tol, 0)
+    assert not bad.any(), (f"{where}: {bad.sum()} scores off; worst err {err.max():.3e}")
+    return float(err.max())
+
+
+def check_attention(gpu_out, ref_out, bf16: bool, where=""):
+    d = np.abs(np.asarray(gpu_out, np.float64) - np.asarray(ref_out, np.float64))
+    if bf16:
+        assert d.max() <= BF16_MAX_ABS, f"{where}: max abs err {d.max():.3e}"
+        assert d.mean() <= BF16_MEAN_ABS, f"{where}: mean abs err {d.mean():.3e}"
+    else:
+        assert d.max() <= F32_MAX_ABS, f"{where}: max abs err {d.max():.3e}"
+    return float(d.max()), float(d.mean())
+
+
+def check_lse(gpu_lse, ref_lse, bf16: bool, where=""):
+    g = np.asarray(gpu_lse, np.float64)
+    r = np.asarray(ref_lse, np.float64)
+    assert np.array_equal(np.isneginf(g), np.isneginf(r)), f"{where}: lse -inf pattern differs"
+    fin = ~np.isneginf(r)
+    tol = 2e-2 if bf16 else 1e-5
+    err = np.abs(g[fin] - r[fin]).max() if fin.any() else 0.0
+    assert err <= tol, f"{where}: lse err {err:.3e}"
+    return float(err)
+
+
+def sample_rows(T, k, rng, extra=6):
+    """Rows to check at full size: first, last, around k, and random ones."""
+    rows = {0, T - 1}
+    for t in (k - 2, k - 1, k, k + 1):
+        if 0 <= t < T:
+            rows.add(t)
+    rows.update(int(x) for x in rng.integers(0, T, extra))
+    return sorted(rows)

@@ -1,0 +1,65 @@
+"""GPU parity of dsa_topk_select: bit-exact against the oracle's selection
+on the very same fp32 score rows."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_02_amd as dsa
+import oracle
+from dsa_parity import gpu_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(scores_cpu, k, q_offset, where):
+    dev = gpu_device()
+    print(f"[topk] {where}", flush=True)
+    got = dsa.topk_select(scores_cpu.to(dev), k, q_offset).cpu().numpy()
+    ref = oracle.topk_select(scores_cpu.double().numpy(), k, q_offset)
+    bad = np.flatnonzero((got != ref).any(axis=-1).ravel())
+    assert bad.size == 0, f"{where}: {bad.size} rows differ, first row {bad[0]}"
+
+
+def _gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+@pytest.mark.parametrize("B,T,N,k,q_offset", [
+    (1, 64, 5000, 2048, 4936),      # chunk-like rows, many thousands of candidates
+    (2, 40, 3001, 512, 2961),       # N not a multiple of 4 (scalar loads)
+    (1, 300, 300, 64, 0),           # prefill: rows with fewer than k candidates
+    (3, 1, 131072, 2048, 131071),   # decode-length rows
+    (1, 8, 4000, 1, 3992),          # k = 1
+])
+def test_random_rows(B, T, N, k, q_offset):
+    s = torch.randn(B, T, N, generator=_gen(N + k)).abs()
+    _check(s, k, q_offset, f"random B={B} T={T} N={N} k={k}")
+
+
+def test_ties_zeros_signed_zero_nan():
+    g = _gen(5)
+    T, N = 32, 6000
+    s = torch.randint(0, 4, (1, T, N), generator=g).float() * 0.5  # heavy exact ties
+    s[torch.rand(1, T, N, generator=g) < 0.3] = 0.0
+    s[torch.rand(1, T, N, generator=g) < 0.1] = -0.0
+    s[torch.rand(1, T, N, generator=g) < 0.02] = float("nan")
+    s[0, 3] = float("nan")                     # a row of NaN only
+    _check(s, 2048, N - T, "ties")
+
+
+def test_one_bin_overflow_fallback():
+    """Scores that share their top 12 key bits overflow the LDS candidate list
+    and take the HBM fallback."""
+    g = _gen(6)
+    s = 1.0 + torch.rand(1, 8, 20000, generator=g) * 0.1
+    s[0, 1] = 0.25                               # all equal
+    s[0, 2, ::3] = 1.0                           # many exact ties at the threshold
+    _check(s, 2048, 20000 - 8, "one-bin")
+
+
+def test_negative_and_infinite_scores():
+    g = _gen(7)
+    s = torch.randn(1, 16, 4096, generator=g)
+    s[0, :, ::17] = float("-inf")
+    s[0, :, ::29] = float("inf")
+    _check(s, 300, 4096 - 16, "signed")
