@@ -34,35 +34,50 @@ namespace dsa {
 namespace {
 
 constexpr int H = 128, DQK = 576, DV = 512;
-constexpr int NWV = 8;                   // waves per workgroup, 16 heads each
-constexpr int NTA = NWV * 64;            // 512 threads
+constexpr int NWV = 4;                   // waves per workgroup, 32 heads each
+constexpr int NTA = NWV * 64;            // 256 threads
 constexpr int TK = 32;                   // keys per tile
-constexpr int KROW = DQK * 2 + 16;       // LDS bytes per key row (padded)
-constexpr int VROW = TK * 2 + 8;         // LDS bytes per V^T row (padded)
-constexpr int KBUF = TK * KROW;          // 37376 B
-constexpr int VBUF = DV * VROW;          // 36864 B
+constexpr int LAT = 1024;                // latent bytes per row (512 bf16)
+constexpr int ROPE = 128;                // rope bytes per row (64 bf16)
+constexpr int STAGE = TK * (LAT + ROPE); // 36 KiB per ring stage
 constexpr int SLOTS = 2048;              // max index slots per workgroup
-constexpr float RESCALE_GAP = 8.0f;      // lazy rescale threshold (log2 units)
+constexpr float REF_GAP = 64.0f;         // max log2 gap above the reference max
+constexpr int DMA_PER_TILE = 9;          // direct-to-LDS loads per wave and tile
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Row swizzle of the 16-byte chunks of a latent row: chunk c of tile row r
+// sits in slot c ^ swz(r).  Eight consecutive rows read at one chunk hit
+// eight different slots (the QK^T fragment reads), and the four rows x two
+// chunks a 16-lane group touches in a transposed read are distinct as well.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& x) {
-    return __builtin_bit_cast(bf16x8, x);
-}
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
-__device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
+// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
+#define DSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 template <bool PARTIAL>
-__global__ __launch_bounds__(NTA) void sparse_mla_attn_bf16(
+__global__ __launch_bounds__(NTA) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_mla_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, int T, int N, int k, int slots_per_split, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (KBUF + VBUF)];
+    // four ring stages, separate objects so that the compiler can tell the
+    // stage being read from the stages being filled
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
     __shared__ int32_t sidx[SLOTS];
     __shared__ int s_last;
+    __shared__ int s_redo;
 
     const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
     const int nsplit = gridDim.x;
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(NTA) void sparse_mla_attn_bf16(
     const int nslots = max(0, min(k - slot0, slots_per_split));
     const uint16_t* __restrict__ kv_b = kv + (size_t)b * N * DQK;
 
-    // ---- slot indices of this workgroup; find the last valid one
+    // ---- slot indices of this workgroup; the last valid one
     if (tid == 0) s_last = -1;
     __syncthreads();
     int my_last = -1;
@@ -84,212 +99,287 @@ __global__ __launch_bounds__(NTA) void sparse_mla_attn_bf16(
     }
     if (my_last >= 0) atomicMax(&s_last, my_last);
 
-    // ---- this wave's 16 query heads, kept as B operands (k = 8*(l/16)+j)
-    bf16x8 qf[DQK / 32];
-    {
-        const uint16_t* qh = q + (row * H + 16 * wave + m) * DQK + 8 * g;
+    // ---- this wave's 32 query heads (two blocks of 16) as B operands
+    // (k = 8*(l/16)+j within each 32-wide step of d)
+    bf16x8 qf[2][DQK / 32];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const uint16_t* qh = q + (row * H + 32 * wave + 16 * hb + m) * DQK + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < DQK / 32; ++ks)
-            qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
+            qf[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
     }
     __syncthreads();
-    const int n_tiles = (s_last + TK) / TK;  // 0 when no slot is valid
+    const int last = s_last;
+    const int n_tiles = (last + TK) / TK;  // 0 when no slot is valid
+    // rows of invalid slots are loaded from a selected row (their weight is 0)
+    const int dummy = last >= 0 ? sidx[last] : 0;
 
-    f32x4 o[DV / 16];
-#pragma unroll
-    for (int i = 0; i < DV / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -__builtin_inff();  // running reference max of head m (log2 units)
-    float l_part = 0.f;               // this lane's part of head m's exp-sum
+    // Softmax without rescaling the accumulator: the reference max m_ref of
+    // head 16*hb + m is the max of the first tile with a valid key, and
+    // later exponentials exp2(x - m_ref) may grow up to 2^REF_GAP, which fp32
+    // accumulators and bf16 weights hold without loss of relative precision.
+    // A tile that exceeds the reference by more than REF_GAP flags the
+    // workgroup, which then reruns the pass with m_ref = the exact max it
+    // recorded (so every exponential is <= 1).
+    f32x4 o[2][DV / 16];
+    float m_ref[2], m_all[2], l_part[2];
+    bool over = false;
+    if (tid == 0) s_redo = 0;
 
-    // gather roles: latent chunk c (8 columns) of keys 4*kg..4*kg+3; rope
-    // chunk rc of key rk (threads < 256)
-    const int c = tid & 63, kg = tid >> 6;
-    const int rk = tid >> 3, rc = 64 + (tid & 7);
-    uint4 lat[4], rope;
-    auto fetch = [&](int tile) {
-        const uint4 zero = {0u, 0u, 0u, 0u};
+    // per-lane LDS offsets inside a stage (all rows use the same swizzle of
+    // their low four bits, so these hold for every tile).  QK^T: chunk
+    // 4*ks + g of row r sits in slot 4*(ks ^ (swz>>2)) + (g ^ (swz&3)).
+    int qk_off[4];
+    {
+        const int sw = swz(m);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int sl = tile * TK + 4 * kg + u;
-            const int id = sl < nslots ? sidx[sl] : -1;
-            lat[u] = (id >= 0 && id < N)
-                         ? *reinterpret_cast<const uint4*>(kv_b + (size_t)id * DQK + 8 * c) : zero;
-        }
-        if (tid < 256) {
-            const int sl = tile * TK + rk;
-            const int id = sl < nslots ? sidx[sl] : -1;
-            rope = (id >= 0 && id < N)
-                       ? *reinterpret_cast<const uint4*>(kv_b + (size_t)id * DQK + 8 * rc) : zero;
-        }
-    };
-    auto stage = [&](int buf) {
-        uint8_t* kb = lds + buf * (KBUF + VBUF);
-        uint8_t* vb = kb + KBUF;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<uint4*>(kb + (4 * kg + u) * KROW + 16 * c) = lat[u];
-        if (tid < 256) *reinterpret_cast<uint4*>(kb + rk * KROW + 16 * rc) = rope;
-        // V^T: column 8c+j holds keys 4kg..4kg+3 contiguously
-        const uint32_t* L0 = reinterpret_cast<const uint32_t*>(&lat[0]);
-        const uint32_t* L1 = reinterpret_cast<const uint32_t*>(&lat[1]);
-        const uint32_t* L2 = reinterpret_cast<const uint32_t*>(&lat[2]);
-        const uint32_t* L3 = reinterpret_cast<const uint32_t*>(&lat[3]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int dw = j >> 1;
-            uint2 v;
-            if (j & 1) {
-                v.x = hi16(L0[dw]) | (L1[dw] & 0xffff0000u);
-                v.y = hi16(L2[dw]) | (L3[dw] & 0xffff0000u);
-            } else {
-                v.x = lo16(L0[dw]) | (L1[dw] << 16);
-                v.y = lo16(L2[dw]) | (L3[dw] << 16);
-            }
-            *reinterpret_cast<uint2*>(vb + (8 * c + j) * VROW + 8 * kg) = v;
-        }
-    };
-
-    if (n_tiles > 0) {
-        fetch(0);
-        stage(0);
+        for (int b2 = 0; b2 < 4; ++b2)
+            qk_off[b2] = m * LAT + 16 * (4 * (b2 ^ (sw >> 2)) + (g ^ (sw & 3)));
     }
-    __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
-        const bool more = it + 1 < n_tiles;
-        if (more) fetch(it + 1);  // in flight while this tile is multiplied
-        const uint8_t* kb = lds + buf * (KBUF + VBUF);
-        const uint8_t* vb = kb + KBUF;
+    const int rope_off = TK * LAT + m * ROPE + 16 * (g ^ (m & 7));
+    // P V: the K order of the MFMA is {4g..4g+3, 16+4g..16+4g+3} on both
+    // operands.  V comes from the latent rows by transposed reads: lane m of
+    // group g reads 8 bytes of row r = 4g + m/4 (and r + 16) at columns
+    // 16*nv + 4*(m%4), i.e. chunk 2*nv + (m%4)/2, and receives column
+    // 16*nv + m of those four rows.  Slot (2*nv + ch) ^ swz(r) splits into
+    // 32*((nv%8) ^ (swz>>1)) + 16*(ch ^ (swz&1)) + 256*(nv/8).
+    // (row r + 16 has the same swizzle, 16 KiB further on)
+    int tr_off[8];
+    {
+        const int r = 4 * g + (m >> 2);
+        const int sw = swz(r), ch = (m & 3) >> 1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            tr_off[j] = r * LAT + 32 * (j ^ (sw >> 1)) + 16 * (ch ^ (sw & 1)) + 8 * (m & 1);
+    }
 
-        // S^T for keys 16*nb + 4*g + i, head m
-        f32x4 st[2];
+    // direct-to-LDS gather of one tile: wave w brings latent rows 8w..8w+7
+    // (one 1 KiB row per instruction, lane l fetching chunk l ^ swz(r)) and
+    // the rope parts of rows 8w..8w+7 (lane l: row 8w+l/8, chunk
+    // (l%8) ^ (row%8)); 9 loads per wave and tile
+    auto issue = [&](uint8_t* st, int tile) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = 8 * wave + u;
+            const int sl = tile * TK + r;
+            int id = sl < nslots ? sidx[sl] : -1;
+            if (id < 0 || id >= N) id = dummy;
+            const uint16_t* src = kv_b + (size_t)id * DQK + 8 * (lane ^ swz(r));
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + r * LAT), 16, 0, 0);
+        }
+        {
+            const int r = 8 * wave + (lane >> 3);
+            const int sl = tile * TK + r;
+            int id = sl < nslots ? sidx[sl] : -1;
+            if (id < 0 || id >= N) id = dummy;
+            const uint16_t* src = kv_b + (size_t)id * DQK + 512 + 8 * ((lane & 7) ^ (r & 7));
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + TK * LAT + wave * 1024), 16, 0, 0);
+        }
+    };
+
+    auto compute = [&](const uint8_t* st, int tile) {
+        // S^T[key, head] for keys 16*nb + 4*g + i, heads 16*hb + m
+        f32x4 sacc[2][2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* kr = kb + (16 * nb + m) * KROW + 16 * g;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < DQK / 32; ++ks)
-                acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(kr + 64 * ks)), qf[ks], acc);
-            st[nb] = acc;
+            for (int ks = 0; ks < 16; ++ks) {
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
+                    st + nb * 16 * LAT + qk_off[ks & 3] + 256 * (ks >> 2)));
+                a0 = mfma_bf16(kf, qf[0][ks], a0);
+                a1 = mfma_bf16(kf, qf[1][ks], a1);
+            }
+#pragma unroll
+            for (int ks = 16; ks < 18; ++ks) {
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
+                    st + rope_off + nb * 16 * ROPE + 64 * (ks - 16)));
+                a0 = mfma_bf16(kf, qf[0][ks], a0);
+                a1 = mfma_bf16(kf, qf[1][ks], a1);
+            }
+            sacc[nb][0] = a0;
+            sacc[nb][1] = a1;
         }
-        // validity and tile max of head m
-        float x[2][4];
-        float mx = -__builtin_inff();
+        bool ok[8];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int sl = it * TK + 16 * nb + 4 * g + i;
+                const int sl = tile * TK + 16 * nb + 4 * g + i;
                 const int id = sl < nslots ? sidx[sl] : -1;
-                const bool ok = id >= 0 && id < N;
-                x[nb][i] = ok ? st[nb][i] * scale_log2 : -__builtin_inff();
-                mx = fmaxf(mx, x[nb][i]);
+                ok[4 * nb + i] = id >= 0 && id < N;
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (__any(mx > m_ref + RESCALE_GAP)) {
-            const float m_new = fmaxf(m_ref, mx);
-            const float alpha = exp2f(m_ref - m_new);
-            l_part *= alpha;
-            float ao[4];
+        bf16x8 pa[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ao[i] = __shfl(alpha, 4 * g + i, 64);
+        for (int hb = 0; hb < 2; ++hb) {
+            float x[8];
+            float mx = -__builtin_inff();
 #pragma unroll
-            for (int nv = 0; nv < DV / 16; ++nv)
+            for (int i = 0; i < 8; ++i) {
+                x[i] = ok[i] ? sacc[i >> 2][hb][i & 3] * scale_log2 : -__builtin_inff();
+                mx = fmaxf(mx, x[i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            m_all[hb] = fmaxf(m_all[hb], mx);
+            if (m_ref[hb] == -__builtin_inff()) m_ref[hb] = mx;  // O and l are still 0
+            else over |= mx > m_ref[hb] + REF_GAP;
+            float p[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[nv][i] *= ao[i];
-            m_ref = m_new;
+            for (int i = 0; i < 8; ++i) {
+                p[i] = ok[i] ? exp2f(x[i] - m_ref[hb]) : 0.f;
+                l_part[hb] += p[i];
+            }
+            pa[hb] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                            (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
         }
-        float p[8];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = x[nb][i] == -__builtin_inff() ? 0.f : exp2f(x[nb][i] - m_ref);
-                p[4 * nb + i] = e;
-                l_part += e;
-            }
-        const bf16x8 pa = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                           (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-        // O += P V, key order {4g..4g+3, 16+4g..16+4g+3} on both operands
 #pragma unroll
         for (int nv = 0; nv < DV / 16; ++nv) {
-            const uint8_t* vr = vb + (16 * nv + m) * VROW + 8 * g;
-            const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 32);
-            const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
-            o[nv] = mfma_bf16(pa, as_bf16x8(vv), o[nv]);
+            const int j = nv & 7, hi = 256 * (nv >> 3);
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + tr_off[j] + hi));
+            const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(st + tr_off[j] + hi + 16 * LAT));
+            const uint4 vv = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1)),
+                              __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3)),
+                              __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 0, 1)),
+                              __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 2, 3))};
+            const bf16x8 vf = as_bf16x8(vv);
+            o[0][nv] = mfma_bf16(pa[0], vf, o[0][nv]);
+            o[1][nv] = mfma_bf16(pa[1], vf, o[1][nv]);
         }
-        if (more) stage(buf ^ 1);
+    };
+
+    // one ring step: wait for tile `it`, publish it with a barrier (which
+    // also tells every wave that the stage read at it-1 is free), refill that
+    // stage with tile it+3, then multiply tile it
+    auto step = [&](uint8_t* cur, uint8_t* nxt, int it) {
+        if (it >= n_tiles) return;
+        const int after = min(2, n_tiles - 1 - it);
+        if (after >= 2) DSA_WAIT_VM(2 * DMA_PER_TILE);
+        else if (after == 1) DSA_WAIT_VM(DMA_PER_TILE);
+        else DSA_WAIT_VM(0);
+        // a barrier that is also a compiler memory barrier (no LDS access moves
+        // across it) but, unlike __syncthreads(), waits for no other loads
+        asm volatile("s_barrier" ::: "memory");
+        if (it + 3 < n_tiles) issue(nxt, it + 3);
+        compute(cur, it);
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+            for (int i = 0; i < DV / 16; ++i) o[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            l_part[hb] = 0.f;
+            m_ref[hb] = pass == 0 ? -__builtin_inff() : m_all[hb];
+            if (pass == 0) m_all[hb] = -__builtin_inff();
+        }
+        if (n_tiles > 0) issue(st0, 0);
+        if (n_tiles > 1) issue(st1, 1);
+        if (n_tiles > 2) issue(st2, 2);
+        for (int it = 0; it < n_tiles; it += 4) {
+            step(st0, st3, it);
+            step(st1, st0, it + 1);
+            step(st2, st1, it + 2);
+            step(st3, st2, it + 3);
+        }
+        if (pass == 1) break;
+        if (__any(over) && lane == 0) atomicOr(&s_redo, 1);
         __syncthreads();
+        if (s_redo == 0) break;
     }
 
-    // ---- finish: exp-sum of head m over the wave, then per O row
-    float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    float lo[4];
+    // ---- finish: exp-sums per head, then per O row
+    const int h0 = 32 * wave;
+    float lo[2][4], l_tot[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo[i] = __shfl(l_tot, 4 * g + i, 64);
-    const int h0 = 16 * wave;
+    for (int hb = 0; hb < 2; ++hb) {
+        float lt = l_part[hb] + __shfl_xor(l_part[hb], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        l_tot[hb] = lt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[hb][i] = __shfl(lt, 4 * g + i, 64);
+    }
     if (PARTIAL) {
         const size_t pbase = (row * nsplit + split) * H;
 #pragma unroll
-        for (int nv = 0; nv < DV / 16; ++nv)
+        for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                part_o[(pbase + h0 + 4 * g + i) * DV + 16 * nv + m] = o[nv][i];
-        if (g == 0) {
-            part_ml[(pbase + h0 + m) * 2 + 0] = m_ref;
-            part_ml[(pbase + h0 + m) * 2 + 1] = l_tot;
+            for (int nv = 0; nv < DV / 16; ++nv)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    part_o[(pbase + h0 + 16 * hb + 4 * g + i) * DV + 16 * nv + m] = o[hb][nv][i];
+            if (g == 0) {
+                part_ml[(pbase + h0 + 16 * hb + m) * 2 + 0] = m_ref[hb];
+                part_ml[(pbase + h0 + 16 * hb + m) * 2 + 1] = l_tot[hb];
+            }
         }
         return;
     }
     if (lse != nullptr && g == 0)
-        lse[row * H + h0 + m] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -__builtin_inff();
-    // normalise, stage bf16 rows in LDS (all tile buffers are free now), store 16 B chunks
-    uint16_t* ob = reinterpret_cast<uint16_t*>(lds) + wave * 16 * DV;
-    float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = lo[i] > 0.f ? 1.f / lo[i] : 0.f;
+        for (int hb = 0; hb < 2; ++hb)
+            lse[row * H + h0 + 16 * hb + m] =
+                l_tot[hb] > 0.f ? (m_ref[hb] + log2f(l_tot[hb])) * kLn2 : -__builtin_inff();
+    // normalise, stage the wave's 32 x 512 bf16 block (32 KiB) in its own ring
+    // stage and store it with 16-byte writes
+    __syncthreads();
+    uint8_t* stage = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    uint16_t* ob = reinterpret_cast<uint16_t*>(stage);
 #pragma unroll
-    for (int nv = 0; nv < DV / 16; ++nv)
+    for (int hb = 0; hb < 2; ++hb) {
+        float inv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ob[(4 * g + i) * DV + 16 * nv + m] = __builtin_bit_cast(uint16_t, (__bf16)(o[nv][i] * inv[i]));
+        for (int i = 0; i < 4; ++i) inv[i] = lo[hb][i] > 0.f ? 1.f / lo[hb][i] : 0.f;
+#pragma unroll
+        for (int nv = 0; nv < DV / 16; ++nv)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ob[(16 * hb + 4 * g + i) * DV + 16 * nv + m] =
+                    __builtin_bit_cast(uint16_t, (__bf16)(o[hb][nv][i] * inv[i]));
+    }
     __syncthreads();
     uint16_t* dst = out + (row * H + h0) * DV;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int ch = r * 64 + lane;  // 16-byte chunk of the wave's 16 x 512 block
-        *reinterpret_cast<uint4*>(dst + ch * 8) = *reinterpret_cast<const uint4*>(ob + ch * 8);
+    for (int r = 0; r < 32; ++r) {
+        const int c = r * 64 + lane;  // 16-byte chunk of the wave's block
+        *reinterpret_cast<uint4*>(dst + c * 8) = *reinterpret_cast<const uint4*>(ob + c * 8);
     }
 }
 
-// Merge the per-split (O, max, sum) partials of one query token.
-__global__ __launch_bounds__(DV) void attn_combine(const float* __restrict__ part_o,
-                                                  const float* __restrict__ part_ml,
-                                                  uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                  int nsplit) {
+// Merge the per-split (O, max, sum) partials: one thread per 4 output
+// columns of one head, 4 heads per workgroup.
+__global__ __launch_bounds__(512) void attn_combine(const float* __restrict__ part_o,
+                                                   const float* __restrict__ part_ml,
+                                                   uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                   int nsplit) {
     const size_t row = blockIdx.x;
-    const int v = threadIdx.x;
-    for (int h = 0; h < H; ++h) {
-        float M = -__builtin_inff();
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((row * nsplit + s) * H + h) * 2]);
-        float L = 0.f, acc = 0.f;
-        if (M != -__builtin_inff()) {
-            for (int s = 0; s < nsplit; ++s) {
-                const size_t pb = (row * nsplit + s) * H + h;
-                const float ms = part_ml[pb * 2];
-                if (ms == -__builtin_inff()) continue;
-                const float f = exp2f(ms - M);
-                L += part_ml[pb * 2 + 1] * f;
-                acc += part_o[pb * DV + v] * f;
-            }
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 7);
+    const int v = (threadIdx.x & 127) * 4;
+    float M = -__builtin_inff();
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((row * nsplit + s) * H + h) * 2]);
+    float L = 0.f;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -__builtin_inff()) {
+        for (int s = 0; s < nsplit; ++s) {
+            const size_t pb = (row * nsplit + s) * H + h;
+            const float ms = part_ml[pb * 2];
+            if (ms == -__builtin_inff()) continue;
+            const float f = exp2f(ms - M);
+            L += part_ml[pb * 2 + 1] * f;
+            const float4 x = *reinterpret_cast<const float4*>(part_o + pb * DV + v);
+            acc.x += x.x * f; acc.y += x.y * f; acc.z += x.z * f; acc.w += x.w * f;
         }
-        const float o = L > 0.f ? acc / L : 0.f;
-        out[(row * H + h) * DV + v] = __builtin_bit_cast(uint16_t, (__bf16)o);
-        if (lse != nullptr && v == 0) lse[row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 pk;
+    pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.x * inv)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.y * inv)) << 16);
+    pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.z * inv)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(out + (row * H + h) * DV + v) = pk;
+    if (lse != nullptr && v == 0) lse[row * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
 }
 
 // ---------------------------------------------------------------------------
@@ -400,7 +490,7 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
         qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, per, scale_log2);
     dsa_status st = launch_status();
     if (st != DSA_OK) return st;
-    attn_combine<<<dim3((unsigned)rows), DV, 0, stream>>>(part_o, part_ml, oo, lse, s_eff);
+    attn_combine<<<dim3((unsigned)rows, H / 4), 512, 0, stream>>>(part_o, part_ml, oo, lse, s_eff);
     return launch_status();
 }
 

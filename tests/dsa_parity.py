@@ -11,8 +11,14 @@ Comparison rules
 * attention outputs: the oracle recomputes attention on the GPU's own index
   set; bf16 must be within 2e-2 max-abs and 5e-3 mean-abs, fp32 within 1e-5
   max-abs;
-* index scores: |gpu - oracle| <= 1e-5 |oracle| + 1e-6 max|oracle row| (fp32
-  accumulation of exact FP8 products, then an 8-term fp32 weighted sum).
+* index scores: |gpu - oracle| <= c * S_abs + 2^-20 |oracle|, where
+  S_abs[t,s] = sum_j |w q_scale|_j k_scale_s sum_d |q8_jd k8_d| is the sum of
+  the magnitudes the dot products add up.  For FP8, c = 2^-14: gfx950's
+  e4m3 MFMA sums the 128 exact products with truncation relative to the
+  largest of them (measured: 65536 + 1 -> 65536; worst random-dot error
+  6.4e-6 = 2^-17.3 of the magnitude sum), so the bound keeps a factor 8 of
+  margin.  For the fp32 path, c = 2^-18 (a 32-term fp32 dot plus the head
+  sum).
 """
 from __future__ import annotations
 
@@ -77,19 +83,27 @@ def check_index_set(gpu_row, oracle_scores_row, oracle_sel, k, n_cand, where="")
     return False
 
 
-def check_scores(gpu, ref, where=""):
+def abs_score_sum(q_idx, k_idx, w, q_scale=None, k_scale=None):
+    """S_abs[b,t,s] = sum_j |w_j| * (|Q_j| . |K_s|) with dequantised operands."""
+    import oracle
+    Q = np.abs(oracle.dequantize(q_idx, q_scale) if q_scale is not None else np.asarray(q_idx, np.float64))
+    K = np.abs(oracle.dequantize(k_idx, k_scale) if k_scale is not None else np.asarray(k_idx, np.float64))
+    W = np.abs(np.asarray(w, np.float64))
+    return np.einsum("btj,btjd,bsd->bts", W, Q, K, optimize=True)
+
+
+def check_scores(gpu, ref, s_abs, coeff, where=""):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape
     ninf_g, ninf_r = np.isneginf(gpu), np.isneginf(ref)
     assert np.array_equal(ninf_g, ninf_r), f"{where}: -inf pattern differs"
     fin = ~ninf_r
-    rowmax = np.max(np.where(fin, np.abs(ref), 0), axis=-1, keepdims=True)
-    tol = 1e-5 * np.abs(ref) + 1e-6 * rowmax
+    tol = coeff * s_abs + 2.0 ** -20 * np.abs(np.where(fin, ref, 0))
     err = np.abs(np.where(fin, gpu - ref, 0))
     bad = err > np.where(fin, tol, 0)
     assert not bad.any(), (f"{where}: {bad.sum()} scores off; worst err {err.max():.3e}")
-    return float(err.max())
+    return float((err / np.maximum(np.where(fin, s_abs, 1), 1e-300)).max())
 
 
 def check_attention(gpu_out, ref_out, bf16: bool, where=""):

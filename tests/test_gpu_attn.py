@@ -76,3 +76,25 @@ def test_bf16_junk_and_empty_rows():
     idx = _random_idx(1, 300, 900, 64, rng, junk=True)
     idx[0, 7] = -1
     _run(wl, idx, 5, "bf16 junk/empty, unsplit")
+
+
+@pytest.mark.parametrize("T", [2, 300])
+def test_bf16_large_logit_gap_reruns_exactly(T):
+    """A selected key in a late tile whose rope part is scaled x80 lifts some
+    heads' logits far above the first tile's max (more than 2^64 in exp2
+    terms); the kernel must notice and redo the pass with the exact max."""
+    dev = gpu_device()
+    wl = WORKLOADS["prefill_8k"].with_(B=1, T=T, N=3000, k=2048 if T == 2 else 256)
+    rng = np.random.default_rng(21)
+    idx = _random_idx(1, T, wl.N, wl.k, rng)
+    inp = make_inputs(wl, seed=8, device="cpu")
+    hot = int(idx[0, 0, wl.k - 5])
+    inp["kv"][0, hot, 512:] *= 80
+    q, kv = inp["q"].to(dev), inp["kv"].to(dev)
+    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx).to(dev), wl.d_v, wl.sm_scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.sparse_mqa_attention(np64(inp["q"]), np64(inp["kv"]), idx, wl.d_v, wl.sm_scale)
+    gap = (ref_l[0, 0] - ref_l[0, 0].min()).max()
+    print(f"  large-gap T={T}: lse spread {gap:.1f}", flush=True)
+    check_attention(np64(out), ref_o, True, f"large gap T={T}")
+    check_lse(np64(lse), ref_l, True, f"large gap T={T}")

@@ -5,7 +5,7 @@ import torch
 
 import long_context_02_amd as dsa
 import oracle
-from dsa_parity import check_scores, gpu_device, np64, to_device
+from dsa_parity import abs_score_sum, check_scores, gpu_device, np64, to_device
 from long_context_02_amd.synth import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -18,9 +18,14 @@ def _run_and_check(wl, seed, dev, where):
     got = dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
                              q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
     torch.cuda.synchronize()
-    ref = oracle.index_scores(np64(inp["q_idx"]), np64(inp["k_idx"]), np64(inp["w"]), wl.q_offset,
-                              q_scale=np64(inp["q_idx_scale"]), k_scale=np64(inp["k_idx_scale"]))
-    return check_scores(got.cpu().numpy(), ref, where)
+    args = (np64(inp["q_idx"]), np64(inp["k_idx"]), np64(inp["w"]))
+    scales = dict(q_scale=np64(inp["q_idx_scale"]), k_scale=np64(inp["k_idx_scale"]))
+    ref = oracle.index_scores(*args, wl.q_offset, **scales)
+    s_abs = abs_score_sum(*args, **scales)
+    coeff = 2.0 ** -14 if wl.dtype == "bf16" else 2.0 ** -18
+    worst = check_scores(got.cpu().numpy(), ref, s_abs, coeff, where)
+    print(f"  {where}: worst |err| / S_abs = {worst:.3e}", flush=True)
+    return worst
 
 
 def test_tiny_f32_full():
@@ -65,7 +70,8 @@ def test_negative_weights():
     g = to_device(inp, dev)
     got = dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], 0, q_idx_scale=g["q_idx_scale"],
                              k_idx_scale=g["k_idx_scale"])
-    ref = oracle.index_scores(np64(inp["q_idx"]), np64(inp["k_idx"]), np64(inp["w"]), 0,
-                              q_scale=np64(inp["q_idx_scale"]), k_scale=np64(inp["k_idx_scale"]))
+    args = (np64(inp["q_idx"]), np64(inp["k_idx"]), np64(inp["w"]))
+    scales = dict(q_scale=np64(inp["q_idx_scale"]), k_scale=np64(inp["k_idx_scale"]))
+    ref = oracle.index_scores(*args, 0, **scales)
     assert (ref[np.isfinite(ref)] < 0).any()
-    check_scores(got.cpu().numpy(), ref, "negative w")
+    check_scores(got.cpu().numpy(), ref, abs_score_sum(*args, **scales), 2.0 ** -14, "negative w")
