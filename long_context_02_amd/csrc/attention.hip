@@ -137,7 +137,10 @@ void sparse_mla_attn_bf16(
         for (int b2 = 0; b2 < 4; ++b2)
             qk_off[b2] = m * LAT + 16 * (4 * (b2 ^ (sw >> 2)) + (g ^ (sw & 3)));
     }
-    const int rope_off = TK * LAT + m * ROPE + 16 * (g ^ (m & 7));
+    // rope chunk 4*a + g (a = 0, 1) of row r sits in slot (4*a + g) ^ (r % 8)
+    int rope_off[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) rope_off[a] = TK * LAT + m * ROPE + 16 * ((4 * a + g) ^ (m & 7));
     // P V: the K order of the MFMA is {4g..4g+3, 16+4g..16+4g+3} on both
     // operands.  V comes from the latent rows by transposed reads: lane m of
     // group g reads 8 bytes of row r = 4g + m/4 (and r + 16) at columns
@@ -159,23 +162,21 @@ void sparse_mla_attn_bf16(
     // the rope parts of rows 8w..8w+7 (lane l: row 8w+l/8, chunk
     // (l%8) ^ (row%8)); 9 loads per wave and tile
     auto issue = [&](uint8_t* st, int tile) {
+        // lane l looks up row 8w + l/8 once; the latent loads take the ids of
+        // rows 8w..8w+7 from lanes 0, 8, .., 56
+        const int r = 8 * wave + (lane >> 3);
+        const int sl = tile * TK + r;
+        int id = sl < nslots ? sidx[sl] : -1;
+        if (id < 0 || id >= N) id = dummy;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int r = 8 * wave + u;
-            const int sl = tile * TK + r;
-            int id = sl < nslots ? sidx[sl] : -1;
-            if (id < 0 || id >= N) id = dummy;
-            const uint16_t* src = kv_b + (size_t)id * DQK + 8 * (lane ^ swz(r));
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + r * LAT), 16, 0, 0);
+            const int ru = 8 * wave + u;
+            const int idu = __builtin_amdgcn_readlane(id, 8 * u);
+            const uint16_t* src = kv_b + (size_t)idu * DQK + 8 * (lane ^ swz(ru));
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + ru * LAT), 16, 0, 0);
         }
-        {
-            const int r = 8 * wave + (lane >> 3);
-            const int sl = tile * TK + r;
-            int id = sl < nslots ? sidx[sl] : -1;
-            if (id < 0 || id >= N) id = dummy;
-            const uint16_t* src = kv_b + (size_t)id * DQK + 512 + 8 * ((lane & 7) ^ (r & 7));
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + TK * LAT + wave * 1024), 16, 0, 0);
-        }
+        const uint16_t* src = kv_b + (size_t)id * DQK + 512 + 8 * ((lane & 7) ^ (r & 7));
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + TK * LAT + wave * 1024), 16, 0, 0);
     };
 
     auto compute = [&](const uint8_t* st, int tile) {
@@ -194,7 +195,7 @@ void sparse_mla_attn_bf16(
 #pragma unroll
             for (int ks = 16; ks < 18; ++ks) {
                 const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    st + rope_off + nb * 16 * ROPE + 64 * (ks - 16)));
+                    st + rope_off[ks - 16] + nb * 16 * ROPE));
                 a0 = mfma_bf16(kf, qf[0][ks], a0);
                 a1 = mfma_bf16(kf, qf[1][ks], a1);
             }
@@ -260,8 +261,10 @@ void sparse_mla_attn_bf16(
         else if (after == 1) DSA_WAIT_VM(DMA_PER_TILE);
         else DSA_WAIT_VM(0);
         // a barrier that is also a compiler memory barrier (no LDS access moves
-        // across it) but, unlike __syncthreads(), waits for no other loads
-        asm volatile("s_barrier" ::: "memory");
+        // across it) but, unlike __syncthreads(), waits for no global loads
+        // (its own earlier LDS reads are finished first, so no stage a
+        // wave is still reading gets refilled)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (it + 3 < n_tiles) issue(nxt, it + 3);
         compute(cur, it);
     };
