@@ -75,7 +75,7 @@ void sparse_mla_attn_bf16(
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
-    __shared__ int32_t sidx[SLOTS];
+    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + TK];
     __shared__ int s_last;
     __shared__ int s_redo;
 
@@ -92,8 +92,9 @@ void sparse_mla_attn_bf16(
     if (tid == 0) s_last = -1;
     __syncthreads();
     int my_last = -1;
-    for (int i = tid; i < nslots; i += NTA) {
-        const int id = idx[row * k + slot0 + i];
+    const int nslots_pad = (nslots + TK - 1) / TK * TK;
+    for (int i = tid; i < nslots_pad; i += NTA) {
+        const int id = i < nslots ? idx[row * k + slot0 + i] : -1;
         sidx[i] = id;
         if (id >= 0 && id < N) my_last = i;
     }
@@ -160,57 +161,75 @@ void sparse_mla_attn_bf16(
     // direct-to-LDS gather of one tile: wave w brings latent rows 8w..8w+7
     // (one 1 KiB row per instruction, lane l fetching chunk l ^ swz(r)) and
     // the rope parts of rows 8w..8w+7 (lane l: row 8w+l/8, chunk
-    // (l%8) ^ (row%8)); 9 loads per wave and tile
-    auto issue = [&](uint8_t* st, int tile) {
-        // lane l looks up row 8w + l/8 once; the latent loads take the ids of
-        // rows 8w..8w+7 from lanes 0, 8, .., 56
+    // (l%8) ^ (row%8)); 9 loads per wave and tile.  gather_ids() looks the
+    // rows up (lane l: row 8w + l/8); dma(u) issues load u.
+    auto gather_id = [&](int tile) __attribute__((always_inline)) {
         const int r = 8 * wave + (lane >> 3);
-        const int sl = tile * TK + r;
-        int id = sl < nslots ? sidx[sl] : -1;
+        int id = sidx[tile * TK + r];
         if (id < 0 || id >= N) id = dummy;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        return id;
+    };
+    auto dma = [&](uint8_t* st, int id, int u) __attribute__((always_inline)) {
+        if (u < 8) {
             const int ru = 8 * wave + u;
             const int idu = __builtin_amdgcn_readlane(id, 8 * u);
             const uint16_t* src = kv_b + (size_t)idu * DQK + 8 * (lane ^ swz(ru));
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + ru * LAT), 16, 0, 0);
+        } else {
+            const int r = 8 * wave + (lane >> 3);
+            const uint16_t* src = kv_b + (size_t)id * DQK + 512 + 8 * ((lane & 7) ^ (r & 7));
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + TK * LAT + wave * 1024), 16, 0, 0);
         }
-        const uint16_t* src = kv_b + (size_t)id * DQK + 512 + 8 * ((lane & 7) ^ (r & 7));
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + TK * LAT + wave * 1024), 16, 0, 0);
+    };
+    auto issue = [&](uint8_t* st, int tile) __attribute__((always_inline)) {
+        const int id = gather_id(tile);
+#pragma unroll
+        for (int u = 0; u < DMA_PER_TILE; ++u) dma(st, id, u);
     };
 
-    auto compute = [&](const uint8_t* st, int tile) {
-        // S^T[key, head] for keys 16*nb + 4*g + i, heads 16*hb + m
-        f32x4 sacc[2][2];
+    // Multiply tile `tile` (in stage st); when nxt is not null, the loads of
+    // tile `tile + 3` into nxt are spread over the QK^T steps.
+    auto compute = [&](const uint8_t* st, int tile, uint8_t* nxt) __attribute__((always_inline)) {
+        const int nid = nxt ? gather_id(tile + 3) : 0;
+        // validity of this lane's keys 4g..4g+3 and 16+4g..16+4g+3
+        const int4 ia = *reinterpret_cast<const int4*>(&sidx[tile * TK + 4 * g]);
+        const int4 ib = *reinterpret_cast<const int4*>(&sidx[tile * TK + 16 + 4 * g]);
+
+        // S^T[key, head] for keys 16*nb + 4*g + i, heads 16*hb + m.  Both key
+        // blocks advance together (four independent accumulators); fragments
+        // are loaded two k-steps ahead of the MFMAs that use them.
+        f32x4 sacc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
+                            {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+        auto kfrag = [&](int nb, int ks) __attribute__((always_inline)) -> bf16x8 {
+            const uint8_t* p = ks < 16 ? st + nb * 16 * LAT + qk_off[ks & 3] + 256 * (ks >> 2)
+                                       : st + rope_off[ks - 16] + nb * 16 * ROPE;
+            return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+        };
+        bf16x8 kf[3][2];
+        kf[0][0] = kfrag(0, 0); kf[0][1] = kfrag(1, 0);
+        kf[1][0] = kfrag(0, 1); kf[1][1] = kfrag(1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 16; ++ks) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    st + nb * 16 * LAT + qk_off[ks & 3] + 256 * (ks >> 2)));
-                a0 = mfma_bf16(kf, qf[0][ks], a0);
-                a1 = mfma_bf16(kf, qf[1][ks], a1);
+        for (int ks = 0; ks < 18; ++ks) {
+            const int c = ks % 3;
+            if (ks + 2 < 18) {
+                kf[(ks + 2) % 3][0] = kfrag(0, ks + 2);
+                kf[(ks + 2) % 3][1] = kfrag(1, ks + 2);
             }
-#pragma unroll
-            for (int ks = 16; ks < 18; ++ks) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    st + rope_off[ks - 16] + nb * 16 * ROPE));
-                a0 = mfma_bf16(kf, qf[0][ks], a0);
-                a1 = mfma_bf16(kf, qf[1][ks], a1);
-            }
-            sacc[nb][0] = a0;
-            sacc[nb][1] = a1;
+            sacc[0][0] = mfma_bf16(kf[c][0], qf[0][ks], sacc[0][0]);
+            sacc[0][1] = mfma_bf16(kf[c][0], qf[1][ks], sacc[0][1]);
+            sacc[1][0] = mfma_bf16(kf[c][1], qf[0][ks], sacc[1][0]);
+            sacc[1][1] = mfma_bf16(kf[c][1], qf[1][ks], sacc[1][1]);
+            if (nxt && (ks & 1) == 0 && (ks >> 1) < DMA_PER_TILE) dma(nxt, nid, ks >> 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if (ks + 2 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+        if (nxt) dma(nxt, nid, DMA_PER_TILE - 1);
+
+        const int ids[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
         bool ok[8];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sl = tile * TK + 16 * nb + 4 * g + i;
-                const int id = sl < nslots ? sidx[sl] : -1;
-                ok[4 * nb + i] = id >= 0 && id < N;
-            }
+        for (int i = 0; i < 8; ++i) ok[i] = ids[i] >= 0 && ids[i] < N;
         bf16x8 pa[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -221,11 +240,15 @@ void sparse_mla_attn_bf16(
                 x[i] = ok[i] ? sacc[i >> 2][hb][i & 3] * scale_log2 : -__builtin_inff();
                 mx = fmaxf(mx, x[i]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            // per-lane bookkeeping; the max over the head's four lane groups is
+            // only needed to fix the reference on the first tile with a valid key
+            if (m_ref[hb] == -__builtin_inff()) {
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                m_ref[hb] = mx;  // O and l are still 0
+            }
             m_all[hb] = fmaxf(m_all[hb], mx);
-            if (m_ref[hb] == -__builtin_inff()) m_ref[hb] = mx;  // O and l are still 0
-            else over |= mx > m_ref[hb] + REF_GAP;
+            over |= mx > m_ref[hb] + REF_GAP;
             float p[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -235,8 +258,8 @@ void sparse_mla_attn_bf16(
             pa[hb] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                             (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
         }
-#pragma unroll
-        for (int nv = 0; nv < DV / 16; ++nv) {
+        // P V, V fragments read two steps ahead
+        auto vfrag = [&](int nv) __attribute__((always_inline)) -> bf16x8 {
             const int j = nv & 7, hi = 256 * (nv >> 3);
             const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + tr_off[j] + hi));
             const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -245,16 +268,26 @@ void sparse_mla_attn_bf16(
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 0, 1)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 2, 3))};
-            const bf16x8 vf = as_bf16x8(vv);
-            o[0][nv] = mfma_bf16(pa[0], vf, o[0][nv]);
-            o[1][nv] = mfma_bf16(pa[1], vf, o[1][nv]);
+            return as_bf16x8(vv);
+        };
+        bf16x8 vf[3];
+        vf[0] = vfrag(0);
+        vf[1] = vfrag(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int nv = 0; nv < DV / 16; ++nv) {
+            if (nv + 2 < DV / 16) vf[(nv + 2) % 3] = vfrag(nv + 2);
+            o[0][nv] = mfma_bf16(pa[0], vf[nv % 3], o[0][nv]);
+            o[1][nv] = mfma_bf16(pa[1], vf[nv % 3], o[1][nv]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+            if (nv + 2 < DV / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
     };
 
     // one ring step: wait for tile `it`, publish it with a barrier (which
-    // also tells every wave that the stage read at it-1 is free), refill that
-    // stage with tile it+3, then multiply tile it
-    auto step = [&](uint8_t* cur, uint8_t* nxt, int it) {
+    // also tells every wave that the stage read at it-1 is free), then
+    // multiply tile it while refilling that stage with tile it+3
+    auto step = [&](uint8_t* cur, uint8_t* nxt, int it) __attribute__((always_inline)) {
         if (it >= n_tiles) return;
         const int after = min(2, n_tiles - 1 - it);
         if (after >= 2) DSA_WAIT_VM(2 * DMA_PER_TILE);
@@ -265,8 +298,7 @@ void sparse_mla_attn_bf16(
         // (its own earlier LDS reads are finished first, so no stage a
         // wave is still reading gets refilled)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (it + 3 < n_tiles) issue(nxt, it + 3);
-        compute(cur, it);
+        compute(cur, it, it + 3 < n_tiles ? nxt : nullptr);
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -288,6 +320,11 @@ void sparse_mla_attn_bf16(
             step(st3, st2, it + 3);
         }
         if (pass == 1) break;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {  // per-lane maxima -> max of the head
+            m_all[hb] = fmaxf(m_all[hb], __shfl_xor(m_all[hb], 16, 64));
+            m_all[hb] = fmaxf(m_all[hb], __shfl_xor(m_all[hb], 32, 64));
+        }
         if (__any(over) && lane == 0) atomicOr(&s_redo, 1);
         __syncthreads();
         if (s_redo == 0) break;

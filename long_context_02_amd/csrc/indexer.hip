@@ -180,8 +180,14 @@ __global__ __launch_bounds__(NT) void indexer_fp8_tiled(
 }
 
 // ---------------------------------------------------------------------------
-constexpr int SQ = 4;      // queries per workgroup (stream)
-constexpr int SU = 4;      // 16-key fragments in flight per wave
+#ifndef DSA_STREAM_SU
+#define DSA_STREAM_SU 4
+#endif
+#ifndef DSA_STREAM_WG_TARGET
+#define DSA_STREAM_WG_TARGET 4096
+#endif
+constexpr int SQ = 4;                 // queries per workgroup (stream)
+constexpr int SU = DSA_STREAM_SU;     // 16-key fragments in flight per wave
 
 template <bool FILL>
 __global__ __launch_bounds__(NT) void indexer_fp8_stream(
@@ -299,7 +305,7 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
             indexer_fp8_tiled<false><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
     } else {
         const int nqg = ceil_div(T, SQ);
-        long long kpw = (long long)nqg * B * n_vis / 4096;
+        long long kpw = (long long)nqg * B * n_vis / DSA_STREAM_WG_TARGET;
         kpw = std::max<long long>(1024, std::min<long long>(16384, kpw));
         kpw = (kpw + 64 * SU - 1) / (64 * SU) * (64 * SU);
         dim3 grid(ceil_div(n_vis, kpw), nqg, B);
