@@ -1,5 +1,9 @@
 """GPU parity of dsa_topk_select: bit-exact against the oracle's selection
-on the very same fp32 score rows."""
+on the very same fp32 score rows.
+
+Batches of at most 255 rows take the segmented path (several workgroups per
+row), larger ones one workgroup per row; every case is run both ways by also
+selecting on the rows repeated into a batch of 256 or more."""
 import numpy as np
 import pytest
 import torch
@@ -11,13 +15,22 @@ from dsa_parity import gpu_device
 pytestmark = pytest.mark.gpu
 
 
+ROWS_SEGMENTED = 255
+
+
 def _check(scores_cpu, k, q_offset, where):
     dev = gpu_device()
-    print(f"[topk] {where}", flush=True)
-    got = dsa.topk_select(scores_cpu.to(dev), k, q_offset).cpu().numpy()
+    B, T, _ = scores_cpu.shape
     ref = oracle.topk_select(scores_cpu.double().numpy(), k, q_offset)
-    bad = np.flatnonzero((got != ref).any(axis=-1).ravel())
-    assert bad.size == 0, f"{where}: {bad.size} rows differ, first row {bad[0]}"
+    reps = [1, -(-(ROWS_SEGMENTED + 1) // (B * T))] if B * T <= ROWS_SEGMENTED else [1]
+    for r in reps:
+        print(f"[topk] {where} rows={B * T * r}", flush=True)
+        s = scores_cpu.repeat(r, 1, 1).to(dev)
+        got = dsa.topk_select(s, k, q_offset).cpu().numpy()
+        for c in range(r):
+            g = got[c * B:(c + 1) * B]
+            bad = np.flatnonzero((g != ref).any(axis=-1).ravel())
+            assert bad.size == 0, f"{where} rows={B * T * r}: {bad.size} rows differ, first row {bad[0]}"
 
 
 def _gen(seed):
@@ -55,6 +68,18 @@ def test_one_bin_overflow_fallback():
     s[0, 1] = 0.25                               # all equal
     s[0, 2, ::3] = 1.0                           # many exact ties at the threshold
     _check(s, 2048, 20000 - 8, "one-bin")
+
+
+def test_decode_rows_ties_and_one_bin():
+    """Decode-length rows: a threshold value shared by ~2000 tokens (ties
+    resolved by index), and rows whose threshold bin overflows the segmented
+    path's candidate list."""
+    g = _gen(8)
+    N = 131072
+    s = torch.randint(0, 64, (1, 4, N), generator=g).float() / 8.0
+    s[0, 2] = 0.5                               # one value everywhere
+    s[0, 3] = 1.0 + torch.rand(N, generator=g) * 0.1  # all keys in one bin
+    _check(s, 2048, N - 4, "decode ties")
 
 
 def test_negative_and_infinite_scores():
