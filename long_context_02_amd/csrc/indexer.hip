@@ -17,8 +17,8 @@
 //    keys hit distinct banks) and double-buffered: the next tile's global
 //    loads are in flight while the current tile is multiplied.
 //  * indexer_fp8_stream (T < 16, e.g. decode): the key stream is read once,
-//    so each wave loads its 16-key fragments straight from HBM, four
-//    fragments in flight per wave.
+//    so each wave loads its 16-key fragments straight from HBM (see the
+//    kernel for its own MFMA row layout and store pattern).
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -181,19 +181,30 @@ __global__ __launch_bounds__(NT) void indexer_fp8_tiled(
 
 // ---------------------------------------------------------------------------
 #ifndef DSA_STREAM_SU
-#define DSA_STREAM_SU 4
+#define DSA_STREAM_SU 8
 #endif
 #ifndef DSA_STREAM_WG_TARGET
-#define DSA_STREAM_WG_TARGET 4096
+#define DSA_STREAM_WG_TARGET 8192
 #endif
-constexpr int SQ = 4;                 // queries per workgroup (stream)
-constexpr int SU = DSA_STREAM_SU;     // 16-key fragments in flight per wave
+constexpr int SU = DSA_STREAM_SU;     // 16-key fragments per wave and block
+static_assert(SU % 4 == 0, "fragments are stored in groups of four");
 
-template <bool FILL>
+// Stream kernel.  The 16 MFMA rows are (2 queries x 8 heads), one MFMA per
+// query pair and 16 keys; C lane l holds rows 4*(l/16)+i, i.e. query l/32 of
+// the pair, heads 4*((l/16)&1)+i, and key l%16, so the two head halves of a
+// score meet with one lane exchange (l ^ 16).  NP query pairs per workgroup.
+//
+// Each wave walks blocks of 16*SU consecutive keys (the four waves take
+// turns); the scores of 64 consecutive keys are gathered across lanes into
+// one 256-byte store per query.  Key loads are unconditional (addresses
+// clamped into the visible range; values past it are never stored unmasked)
+// and the next block's loads are issued before this block's stores.
+template <bool FILL, int NP>
 __global__ __launch_bounds__(NT) void indexer_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
     int T, int N, int q_offset, int keys_per_wg) {
+    constexpr int SQ = 2 * NP;
     const int b = blockIdx.z;
     const int tq0 = blockIdx.y * SQ;
     const int s_begin = blockIdx.x * keys_per_wg;
@@ -207,42 +218,87 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
     const uint8_t* __restrict__ k_b = k + (size_t)b * N * DI;
     const float* __restrict__ ks_b = ks + (size_t)b * N;
 
-    i32x8 a[2];
-    float ws[HI];
-    load_queries(q, qs, w, row0, tq0, T, lane, a, ws);
-    const int t = tq0 + kb;
+    // A rows m: query tq0 + 2p + (m >> 3), head m & 7
+    i32x8 a[NP];
+    float ws[NP][4];
+    int tl[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int ta = tq0 + 2 * p + (m >> 3), h = m & 7;
+        if (ta < T) {
+            const uint4* src = reinterpret_cast<const uint4*>(q + ((row0 + ta) * HI + h) * DI + 32 * kb);
+            a[p] = pack8(src[0], src[1]);
+        } else {
+            a[p] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        tl[p] = tq0 + 2 * p + (kb >> 1);  // the query this lane's C rows belong to
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h2 = 4 * (kb & 1) + i;
+            ws[p][i] = tl[p] < T ? w[(row0 + tl[p]) * HI + h2] * qs[(row0 + tl[p]) * HI + h2] : 0.f;
+        }
+    }
 
-    // wave w reads fragments w, w+4, w+8, ... of the workgroup's key range, so
-    // one round of the four waves covers 64*SU consecutive keys
-    for (int base = s_begin + 16 * wave; base < s_vis; base += 64 * SU) {
-        uint4 x0[SU], x1[SU];
-        float kss[SU];
+    uint4 x0[SU], x1[SU];
+    float kss[SU];
+    auto load = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
-            const int s = base + 64 * u + m;
-            if (s < s_vis) {
-                const uint4* p = reinterpret_cast<const uint4*>(k_b + (size_t)s * DI + 32 * kb);
-                x0[u] = p[0];
-                x1[u] = p[1];
-                kss[u] = ks_b[s];
-            } else {
-                x0[u] = x1[u] = uint4{0u, 0u, 0u, 0u};
-                kss[u] = 0.f;
-            }
+            const int s = min(base + 16 * u + m, s_vis - 1);
+            const uint4* p = reinterpret_cast<const uint4*>(k_b + (size_t)s * DI + 32 * kb);
+            x0[u] = p[0];
+            x1[u] = p[1];
+            kss[u] = ks_b[s];
         }
+    };
+    float sc[NP][SU];
+    auto comp = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
-            const int s0 = base + 64 * u;
-            if (s0 < s_vis) {
-                const i32x8 bf = pack8(x0[u], x1[u]);
-                const f32x4 acc0 = mfma_fp8(a[0], bf);
-                const f32x4 acc1 = mfma_fp8(a[1], bf);
-                const int s_abs = s0 + m;
-                float sc = head_sum(acc0, acc1, ws) * kss[u];
-                if (s_abs > q_offset + t) sc = -__builtin_inff();
-                if (t < t_end && s_abs < s_end) out_b[(size_t)t * N + s_abs] = sc;
+            const i32x8 bf = pack8(x0[u], x1[u]);
+            const int s_abs = base + 16 * u + m;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const f32x4 acc = mfma_fp8(a[p], bf);
+                float part = ws[p][0] * fmaxf(acc[0], 0.f);
+                part = fmaf(ws[p][1], fmaxf(acc[1], 0.f), part);
+                part = fmaf(ws[p][2], fmaxf(acc[2], 0.f), part);
+                part = fmaf(ws[p][3], fmaxf(acc[3], 0.f), part);
+                float v = (part + __shfl_xor(part, 16, 64)) * kss[u];
+                if (s_abs > q_offset + tl[p]) v = -__builtin_inff();
+                sc[p][u] = v;
             }
         }
+    };
+    // lane l of group g stores key base + 64g + l: fragment 4g + l/16, key
+    // l%16, read from lane l%16 (first query of the pair) or 32 + l%16
+    auto store = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < SU / 4; ++g) {
+            const int key = base + 64 * g + lane;
+            const bool in = (key & ~15) < s_vis && key < s_end;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) {
+                    const int tq = tq0 + 2 * p + qq;
+                    float v = 0.f;
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        const float x = __shfl(sc[p][4 * g + f], 32 * qq + m, 64);
+                        v = kb == f ? x : v;
+                    }
+                    if (in && tq < t_end) out_b[(size_t)tq * N + key] = v;
+                }
+            }
+        }
+    };
+    int base = s_begin + 16 * SU * wave;
+    if (base < s_vis) load(base);
+    for (; base < s_vis; base += 64 * SU) {
+        comp(base);
+        if (base + 64 * SU < s_vis) load(base + 64 * SU);
+        store(base);
     }
     if (FILL) {
         // fragments cover [s_begin, s_vis) rounded up to 16; fill the rest
@@ -303,16 +359,21 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
             indexer_fp8_tiled<true><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
         else
             indexer_fp8_tiled<false><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+        return launch_status();
+    }
+    const int np = T <= 2 ? 1 : 2;
+    const int nqg = ceil_div(T, 2 * np);
+    long long kpw = (long long)nqg * B * n_vis / DSA_STREAM_WG_TARGET;
+    kpw = std::max<long long>(1024, std::min<long long>(16384, kpw));
+    kpw = (kpw + 64 * SU - 1) / (64 * SU) * (64 * SU);
+    dim3 grid(ceil_div(n_vis, kpw), nqg, B);
+    auto go = [&](auto kern) {
+        kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+    };
+    if (np == 1) {
+        if (fill_masked) go(indexer_fp8_stream<true, 1>); else go(indexer_fp8_stream<false, 1>);
     } else {
-        const int nqg = ceil_div(T, SQ);
-        long long kpw = (long long)nqg * B * n_vis / DSA_STREAM_WG_TARGET;
-        kpw = std::max<long long>(1024, std::min<long long>(16384, kpw));
-        kpw = (kpw + 64 * SU - 1) / (64 * SU) * (64 * SU);
-        dim3 grid(ceil_div(n_vis, kpw), nqg, B);
-        if (fill_masked)
-            indexer_fp8_stream<true><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
-        else
-            indexer_fp8_stream<false><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+        if (fill_masked) go(indexer_fp8_stream<true, 2>); else go(indexer_fp8_stream<false, 2>);
     }
     return launch_status();
 }

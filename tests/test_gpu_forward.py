@@ -73,6 +73,8 @@ def test_tiny_full():
     (1, 600, 600, 0, 256),        # prefill, rows below and above k
     (2, 130, 1500, 1370, 512),    # chunked prefill, ragged
     (5, 1, 3000, 2999, 2048),     # decode, split attention
+    (3, 5, 5000, 4990, 2048),     # few-token decode: two query pairs, a ragged one
+    (2, 3, 2100, 2046, 2048),     # rows with fewer, exactly k and one more candidate
 ])
 def test_mid_sizes_all_rows(B, T, N, q_offset, k):
     dev = gpu_device()
@@ -100,6 +102,26 @@ def test_full_size_sampled(name):
         rows = [(0, t) for t in sample_rows(wl.T, wl.k, rng)]
     _check_rows(wl, g, out, lse, idx, rows, name)
     del g, out, lse, idx
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,B,T", [("decode_128k", 64, 1), ("decode_128k", 4, 2),
+                                      ("chunk_128k", 2, 7)])
+def test_forward_selection_matches_separate_calls(name, B, T):
+    """dsa_forward's selection equals, bit for bit, dsa_topk_select run on
+    dsa_indexer_scores' output: the same score kernel (without the -inf fill
+    of the non-causal part) and the same selection over the workspace."""
+    dev = gpu_device()
+    wl = WORKLOADS[name].with_(B=B, T=T, q_offset=WORKLOADS[name].N - T)
+    print(f"[forward] vs separate calls {name} B={B} T={T}", flush=True)
+    g = make_inputs(wl, seed=5, device=dev)
+    _, _, idx = _forward(wl, g)
+    scores = dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
+                                q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
+    ref = dsa.topk_select(scores, wl.k, wl.q_offset)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref)
+    del g, scores
     torch.cuda.empty_cache()
 
 
