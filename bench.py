@@ -2,6 +2,7 @@
 attention) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_128k]
+    python bench.py --copy-calibration MIB   (a plain device copy, for counters)
 
 A step is one dsa_forward call over one batch of seeded synthetic inputs that
 are already resident in HBM.  The default workload is decode at 128K context:
@@ -9,13 +10,21 @@ are already resident in HBM.  The default workload is decode at 128K context:
 indexer keys [131072,128] and bf16 latent KV [131072,576] per sequence,
 8 indexer heads, k = 2048, 128 query heads, value dim 512).  Prints one JSON
 line; ``value`` is query tokens per second.  The line also carries the
-roofline position of the step's dominant kernel (timed with HIP events on
-the stream it runs on) and the CPU oracle's throughput on a bounded sample
-of the same workload.
+roofline position of the step's dominant kernel and the CPU oracle's
+throughput on a bounded sample of the same workload.
+
+Per-kernel times come from a second timed loop that calls the three entry
+points of the path one after the other (indexer scores -> top-k -> sparse
+attention, the kernels dsa_forward runs) with HIP events recorded between
+them on the stream they are launched on, so each kernel runs in the same
+cache state as inside a step.  The measured HBM traffic of the dominant
+kernel is read from its rocprofv3 counter summary under profiles/ when that
+summary was taken on the current kernel source, else it is null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +44,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "attention": "attention.hip"}
 
 
 def log(*a):
@@ -58,7 +68,8 @@ def work(wl):
     return {
         "indexer": {
             "flops": idx_pairs * 2 * wl.H_I * wl.d_I,
-            "bytes": keys_read * key_bytes + wl.B * wl.T * qrow_bytes,
+            # keys and their scales in, query rows in, one fp32 score out per causal pair
+            "bytes": keys_read * key_bytes + wl.B * wl.T * qrow_bytes + idx_pairs * 4,
             "flop_unit": "fp8" if fp8 else "f32",
         },
         "topk": {"flops": 0, "bytes": idx_pairs * 4 + wl.B * wl.T * wl.k * 4, "flop_unit": None},
@@ -83,6 +94,41 @@ def roofline(phase, w, seconds):
     ach = w["bytes"] / seconds / 1e9
     return {"kernel": phase, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic": w["bytes"]}
+
+
+def measured_traffic(phase, wl):
+    """HBM bytes per launch of `phase` on `wl` from the counter summary in
+    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy calibration),
+    or None when there is none or it was taken on another kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{phase}_{wl.name}_traffic.txt")
+    src = os.path.join(ROOT, "long_context_02_amd", "csrc", KERNEL_SOURCES[phase])
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if "=" in ln and not ln.startswith("#"):
+                key, val = ln.split("=", 1)
+                fields[key.strip()] = val.strip()
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of a known size, for scaling the HBM
+    byte counters (each launch reads and writes mib MiB)."""
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -153,12 +199,17 @@ def main():
     ap.add_argument("--workload", default="decode_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -182,27 +233,41 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     ms = timed(step, args.steps, stream)
 
-    # the three kernels of a step, each timed on its own over the same number of launches
+    # the three kernels of a step: the entry points called in sequence, HIP
+    # events between them on the launch stream
     scores = torch.empty(B, T, N, dtype=torch.float32, device=dev)
     idx = torch.empty(B, T, wl.k, dtype=torch.int32, device=dev)
     attn_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_ATTN, B, T, N, wl.H, wl.d_v, wl.k)),
+                          dtype=torch.uint8, device=dev)
+    topk_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_TOPK, B, T, N, 1, 1, wl.k)),
                           dtype=torch.uint8, device=dev)
     phases = {
         "indexer": lambda: dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
                                               q_idx_scale=g["q_idx_scale"],
                                               k_idx_scale=g["k_idx_scale"], out=scores),
-        "topk": lambda: dsa.topk_select(scores, wl.k, wl.q_offset, out=idx),
+        "topk": lambda: dsa.topk_select(scores, wl.k, wl.q_offset, out=idx, workspace=topk_ws),
         "attention": lambda: dsa.sparse_mla_attn(g["q"], g["kv"], idx, wl.d_v, wl.sm_scale,
                                                  out=out, lse=False, workspace=attn_ws),
     }
-    phase_ms = {}
-    for name, fn in phases.items():
-        fn()
-        phase_ms[name] = timed(fn, args.steps, stream)
+    names = list(phases)
+    for _ in range(args.warmup):
+        for fn in phases.values():
+            fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, name in enumerate(names):
+            phases[name]()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    phase_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, name in enumerate(names)}
     w = work(wl)
     dom = max(phase_ms, key=phase_ms.get)
     roof = roofline(dom, w[dom], phase_ms[dom] / 1e3)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, wl)
 
     line = {
         "metric": "DSA tokens/s (indexer+top-k+sparse attn) at 128K ctx; % of MFMA / HBM roofline",

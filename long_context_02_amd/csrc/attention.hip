@@ -6,28 +6,33 @@
 // rope) per selected token is shared by all 128 query heads, and the value
 // is its 512-wide latent part.
 //
-// bf16 path: one workgroup (8 waves, 16 heads each) per query token and
-// slot range.  Per 32-key tile the selected rows are gathered with 16-byte
-// coalesced loads (a row is 72 chunks: 64 latent + 8 rope) and written to
-// LDS twice: row-major for the key product, and with the latent part
-// transposed (V^T, keys contiguous) for the value product, the transpose
-// done in registers on 4x8 blocks.  Tiles are double-buffered: the next
-// tile's gather is in flight while the current one is multiplied.
+// bf16 path: one workgroup (4 waves, 32 heads each, one wave per SIMD) per
+// query token and slot range.  The selected latent rows are gathered 32 at a
+// time (a tile) straight into LDS with direct-to-LDS loads (global_load_lds;
+// no registers in flight) through a ring of four 36 KiB stages; the loads of
+// tile i+3 are issued between the key-product MFMAs of tile i.  Latent rows
+// are stored with their 16-byte chunks swizzled so that both the key-product
+// fragment reads and the transposed value reads are free of bank conflicts.
 //
 // Per wave and tile:
-//   S^T[key, head] = K[key, :] . Q[head, :]        18 x 2 bf16 MFMA 16x16x32
-//     (A = key rows from LDS, B = the wave's 16 query heads kept in VGPRs;
-//      computing S^T instead of S puts one head per lane column, which is
-//      exactly the row layout the P operand of the value product needs)
-//   online softmax in base 2 with a lazy rescale (the running reference
-//     max only moves when a tile max exceeds it by more than 8, so exp2
-//     stays <= 256 and the O rescale is rare)
-//   O[head, v] += P[head, key] V[key, v]           32 bf16 MFMA 16x16x32
-//     (the key order inside the MFMA's K dimension is permuted to match
-//      the accumulator layout of S^T; V^T is read with the same permutation)
-// The O accumulator (16 heads x 512 fp32) stays in registers.  Decode-sized
-// batches split the slots over several workgroups and merge the partial
-// (O, max, sum) triples in attn_combine.
+//   S^T[key, head] = K[key, :] . Q[head, :]        18 x 4 bf16 MFMA 16x16x32
+//     (A = key rows from LDS, B = the wave's 32 query heads kept in VGPRs;
+//      S^T puts one head per lane column, the layout the P operand of the
+//      value product needs)
+//   softmax in base 2 against a fixed reference max per head (the max of
+//     the first tile with a valid key): exp2(x - m_ref) may grow to
+//     2^REF_GAP, which fp32 sums and bf16 weights carry without loss of
+//     relative precision, so the accumulator is never rescaled; a tile that
+//     exceeds the reference by more than REF_GAP makes the workgroup redo
+//     the pass against the exact max it recorded
+//   O[head, v] += P[head, key] V[key, v]           2 x 32 bf16 MFMA 16x16x32
+//     (V^T fragments come from the latent rows in LDS through ds_read_b64_tr_b16
+//      transposed reads; the key order of the MFMA's K dimension matches the
+//      accumulator layout of S^T)
+// The O accumulator (32 heads x 512 fp32 per wave) lives in AGPRs.  Batches
+// with fewer rows than CUs split the slots over several workgroups; each
+// writes its O rows normalised in bf16 with its per-head (max, exp-sum), and
+// attn_combine merges them.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -67,7 +72,7 @@ template <bool PARTIAL>
 __global__ __launch_bounds__(NTA) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml, int T, int N, int k, int slots_per_split, float scale_log2) {
     // four ring stages, separate objects so that the compiler can tell the
     // stage being read from the stages being filled
@@ -342,26 +347,20 @@ void sparse_mla_attn_bf16(
         for (int i = 0; i < 4; ++i) lo[hb][i] = __shfl(lt, 4 * g + i, 64);
     }
     if (PARTIAL) {
+        // this split's (max, exp-sum) per head; its O rows go out normalised
         const size_t pbase = (row * nsplit + split) * H;
+        if (g == 0)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-            for (int nv = 0; nv < DV / 16; ++nv)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    part_o[(pbase + h0 + 16 * hb + 4 * g + i) * DV + 16 * nv + m] = o[hb][nv][i];
-            if (g == 0) {
+            for (int hb = 0; hb < 2; ++hb) {
                 part_ml[(pbase + h0 + 16 * hb + m) * 2 + 0] = m_ref[hb];
                 part_ml[(pbase + h0 + 16 * hb + m) * 2 + 1] = l_tot[hb];
             }
-        }
-        return;
-    }
-    if (lse != nullptr && g == 0)
+    } else if (lse != nullptr && g == 0) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
             lse[row * H + h0 + 16 * hb + m] =
                 l_tot[hb] > 0.f ? (m_ref[hb] + log2f(l_tot[hb])) * kLn2 : -__builtin_inff();
+    }
     // normalise, stage the wave's 32 x 512 bf16 block (32 KiB) in its own ring
     // stage and store it with 16-byte writes
     __syncthreads();
@@ -380,7 +379,7 @@ void sparse_mla_attn_bf16(
                     __builtin_bit_cast(uint16_t, (__bf16)(o[hb][nv][i] * inv[i]));
     }
     __syncthreads();
-    uint16_t* dst = out + (row * H + h0) * DV;
+    uint16_t* dst = PARTIAL ? part_o + ((row * nsplit + split) * H + h0) * DV : out + (row * H + h0) * DV;
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
         const int c = r * 64 + lane;  // 16-byte chunk of the wave's block
@@ -388,9 +387,10 @@ void sparse_mla_attn_bf16(
     }
 }
 
-// Merge the per-split (O, max, sum) partials: one thread per 4 output
-// columns of one head, 4 heads per workgroup.
-__global__ __launch_bounds__(512) void attn_combine(const float* __restrict__ part_o,
+// Merge the per-split partials (normalised bf16 O rows, max, exp-sum): the
+// split weights are sum_s * 2^(max_s - M).  One thread per 4 output columns
+// of one head, 4 heads per workgroup.
+__global__ __launch_bounds__(512) void attn_combine(const uint16_t* __restrict__ part_o,
                                                    const float* __restrict__ part_ml,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse,
                                                    int nsplit) {
@@ -406,10 +406,13 @@ __global__ __launch_bounds__(512) void attn_combine(const float* __restrict__ pa
             const size_t pb = (row * nsplit + s) * H + h;
             const float ms = part_ml[pb * 2];
             if (ms == -__builtin_inff()) continue;
-            const float f = exp2f(ms - M);
-            L += part_ml[pb * 2 + 1] * f;
-            const float4 x = *reinterpret_cast<const float4*>(part_o + pb * DV + v);
-            acc.x += x.x * f; acc.y += x.y * f; acc.z += x.z * f; acc.w += x.w * f;
+            const float f = part_ml[pb * 2 + 1] * exp2f(ms - M);
+            L += f;
+            const uint2 x = *reinterpret_cast<const uint2*>(part_o + pb * DV + v);
+            acc.x += __uint_as_float(x.x << 16) * f;
+            acc.y += __uint_as_float(x.x & 0xffff0000u) * f;
+            acc.z += __uint_as_float(x.y << 16) * f;
+            acc.w += __uint_as_float(x.y & 0xffff0000u) * f;
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -501,7 +504,7 @@ size_t attn_workspace_bytes(int B, int T, int H_, int d_v, int k, dsa_dtype dtyp
     const long long rows = (long long)B * T;
     const int s = attn_num_splits((int)std::min<long long>(rows, 1 << 30), k);
     if (s <= 1) return 0;
-    return align_up((size_t)rows * s * H_ * d_v * sizeof(float)) +
+    return align_up((size_t)rows * s * H_ * d_v * sizeof(uint16_t)) +
            align_up((size_t)rows * s * H_ * 2 * sizeof(float));
 }
 
@@ -523,9 +526,9 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
     }
     const int per = ((k + s - 1) / s + TK - 1) / TK * TK;
     const int s_eff = (k + per - 1) / per;
-    float* part_o = static_cast<float*>(workspace);
+    uint16_t* part_o = static_cast<uint16_t*>(workspace);
     float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                              align_up((size_t)rows * s * H * DV * sizeof(float)));
+                                              align_up((size_t)rows * s * H * DV * sizeof(uint16_t)));
     sparse_mla_attn_bf16<true><<<dim3(s_eff, T, B), NTA, 0, stream>>>(
         qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, per, scale_log2);
     dsa_status st = launch_status();
