@@ -108,7 +108,11 @@ DSA_API dsa_status dsa_indexer_scores(const void* q_idx, const float* q_idx_scal
  *                       indices in ascending order, then -1 padding
  * Ranking: larger score first; equal scores go to the lower index; -0 equals
  * +0; NaN ranks below every number.  The result is unique and deterministic.
- * workspace may be NULL when dsa_workspace_size(DSA_OP_TOPK, ...) is 0.
+ * Batches of at most 255 rows (B*T <= 255, e.g. decode) are selected by
+ * several workgroups per row and need dsa_workspace_size(DSA_OP_TOPK, ...)
+ * bytes of workspace (per row: a 4096-bin histogram, counters and candidate
+ * lists), which the call overwrites; larger batches need none and workspace
+ * may then be NULL.
  */
 DSA_API dsa_status dsa_topk_select(const float* scores, int32_t* idx,
                            int B, int T, int N, int k, int q_offset,
@@ -132,7 +136,11 @@ DSA_API dsa_status dsa_topk_select(const float* scores, int32_t* idx,
  *  lse [B,T,H] f32 or NULL
  * A row with no valid slot gets out = 0 and lse = -inf.  bf16 runs the
  * products on bf16 MFMA with fp32 logits/softmax/accumulation and rounds the
- * softmax weights to bf16 before the value product.
+ * softmax weights to bf16 before the value product.  bf16 batches with fewer
+ * rows than the GPU has compute units split each row's slots over several
+ * workgroups; the workspace (dsa_workspace_size(DSA_OP_ATTN, ...) bytes,
+ * 16-byte aligned, overwritten) then holds their normalised bf16 partial
+ * outputs and fp32 (max, exp-sum) pairs.
  */
 DSA_API dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx,
                                void* out, float* lse,

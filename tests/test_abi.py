@@ -39,13 +39,18 @@ def test_status_strings_and_version():
 
 
 def test_workspace_sizes():
-    # top-k needs none; forward holds the fp32 score matrix and the indices
+    # top-k needs none for long batches; batches of at most 255 rows hold
+    # a per-row histogram, counters and candidate lists
     assert dsa.workspace_size(dsa.OP_TOPK, 1, 8192, 8192, 128, 512, 2048) == 0
+    seg = dsa.workspace_size(dsa.OP_TOPK, 64, 1, 131072, 128, 512, 2048)
+    assert seg >= 64 * (4096 + 2048 + 2 * 12288) * 4
+    # forward holds the fp32 score matrix and the indices
     fwd = dsa.workspace_size(dsa.OP_FORWARD, 1, 4096, 131072, 128, 512, 2048)
     assert fwd >= 4096 * 131072 * 4 + 4096 * 2048 * 4
-    # decode splits the 2048 slots of its 64 rows over 4 workgroups each
+    # decode splits the 2048 slots of its 64 rows over 4 workgroups each:
+    # bf16 O rows plus fp32 (max, sum) per split and head
     att = dsa.workspace_size(dsa.OP_ATTN, 64, 1, 131072, 128, 512, 2048)
-    assert att >= 64 * 4 * 128 * 512 * 4
+    assert att >= 64 * 4 * 128 * (512 * 2 + 2 * 4)
     # prefill-sized batches need no split workspace; f32 shapes never do
     assert dsa.workspace_size(dsa.OP_ATTN, 1, 8192, 8192, 128, 512, 2048) == 0
     assert dsa.workspace_size(dsa.OP_ATTN, 1, 4, 256, 16, 64, 64) == 0
