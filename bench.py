@@ -54,6 +54,10 @@ def log(*a):
 # ---------------------------------------------------------------------------
 # algorithmic work of one step (what the method must do, not what it skips)
 def work(wl):
+    """Algorithmic FLOP and HBM bytes of each phase: what the method must do,
+    not the dense work it avoids and not the implementation's intermediates
+    (the fp32 score matrix, split partials) -- those show up in the measured
+    traffic instead."""
     t = np.arange(wl.T, dtype=np.int64)
     n_cand = np.minimum(wl.N, wl.q_offset + t + 1)
     n_sel = np.minimum(wl.k, n_cand)
@@ -65,21 +69,32 @@ def work(wl):
     qrow_bytes = wl.H_I * (wl.d_I + 8) if fp8 else wl.H_I * (4 * wl.d_I + 4)
     el = 2 if fp8 else 4
     kv_row = wl.d_qk * el
+    # a selected latent row is read once per query token when the tokens of a
+    # sequence select disjoint rows (decode), and once per sequence when many
+    # tokens share the cache-resident rows (prefill, chunk): at least the
+    # smaller of the two
+    gathered_rows = min(attn_pairs, keys_read)
     return {
         "indexer": {
             "flops": idx_pairs * 2 * wl.H_I * wl.d_I,
-            # keys and their scales in, query rows in, one fp32 score out per causal pair
-            "bytes": keys_read * key_bytes + wl.B * wl.T * qrow_bytes + idx_pairs * 4,
+            "bytes": keys_read * key_bytes + wl.B * wl.T * qrow_bytes,
             "flop_unit": "fp8" if fp8 else "f32",
         },
         "topk": {"flops": 0, "bytes": idx_pairs * 4 + wl.B * wl.T * wl.k * 4, "flop_unit": None},
         "attention": {
             "flops": attn_pairs * 2 * wl.H * (wl.d_qk + wl.d_v),
-            # each selected latent row gathered once per query token, plus Q in and O out
-            "bytes": attn_pairs * kv_row + wl.B * wl.T * wl.H * (wl.d_qk + wl.d_v) * el,
+            "bytes": gathered_rows * kv_row + wl.B * wl.T * (wl.H * (wl.d_qk + wl.d_v) * el + wl.k * 4),
             "flop_unit": "bf16" if fp8 else "f32",
         },
     }
+
+
+def phase_floor(w):
+    """Seconds a phase needs at the published peaks: max(FLOP / MFMA peak, bytes / HBM)."""
+    peak_f = {"fp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_TFLOPS}.get(w["flop_unit"])
+    t_mem = w["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_cmp = w["flops"] / (peak_f * 1e12) if peak_f else 0.0
+    return max(t_mem, t_cmp)
 
 
 def roofline(phase, w, seconds):
@@ -268,6 +283,7 @@ def main():
     dom = max(phase_ms, key=phase_ms.get)
     roof = roofline(dom, w[dom], phase_ms[dom] / 1e3)
     roof["traffic"] = measured_traffic(dom, wl)
+    t_roof = sum(phase_floor(w[p]) for p in w)
 
     line = {
         "metric": "DSA tokens/s (indexer+top-k+sparse attn) at 128K ctx; % of MFMA / HBM roofline",
@@ -288,6 +304,9 @@ def main():
                    "parallelism": "single GPU"},
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "roofline": roof,
+        # the whole step against the sum of the phases' floors at published peaks
+        "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 4),
+                          "frac": round(t_roof / (ms / 1e3), 4)},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
