@@ -9,13 +9,15 @@
 // (4 queries x 4 heads); two MFMAs (heads 0-3 and 4-7) put all 8 head dots
 // of one (query, key) pair in the same lane, so ReLU, the (w * q_scale)
 // weighted head sum and the key scale run in registers with no cross-lane
-// traffic, and each lane stores one finished fp32 score.
+// traffic.
 //
-//  * indexer_fp8_tiled  (T >= 16): a workgroup owns 64 queries (16 per wave)
+//  * indexer_fp8_tiled  (T >= 16): a workgroup owns 64 queries (8 waves x 8)
 //    and a range of keys; 64-key tiles are staged through LDS (rows padded
 //    to 144 B so the 16 lanes that read one 32-byte slice of 16 different
 //    keys hit distinct banks) and double-buffered: the next tile's global
-//    loads are in flight while the current tile is multiplied.
+//    loads are in flight while the current tile is multiplied.  Each wave
+//    collects its 8 x 64 scores in LDS and writes them as whole 256-byte row
+//    segments with 16-byte stores.
 //  * indexer_fp8_stream (T < 16, e.g. decode): the key stream is read once,
 //    so each wave loads its 16-key fragments straight from HBM (see the
 //    kernel for its own MFMA row layout and store pattern).
@@ -43,16 +45,21 @@ __device__ __forceinline__ i32x8 pack8(const uint4& x0, const uint4& x1) {
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
+// ReLU as one integer max on the bit pattern: negative floats (sign bit
+// set, -0 included) are negative as int32 and become +0, the rest pass
+// unchanged.  (fmaxf would add a NaN-quieting max in front of every use.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // sum_j ws[j] * ReLU(D_j): acc0 holds heads 0-3, acc1 heads 4-7.
 __device__ __forceinline__ float head_sum(const f32x4& acc0, const f32x4& acc1, const float* ws) {
-    float s = ws[0] * fmaxf(acc0[0], 0.f);
-    s = fmaf(ws[1], fmaxf(acc0[1], 0.f), s);
-    s = fmaf(ws[2], fmaxf(acc0[2], 0.f), s);
-    s = fmaf(ws[3], fmaxf(acc0[3], 0.f), s);
-    s = fmaf(ws[4], fmaxf(acc1[0], 0.f), s);
-    s = fmaf(ws[5], fmaxf(acc1[1], 0.f), s);
-    s = fmaf(ws[6], fmaxf(acc1[2], 0.f), s);
-    s = fmaf(ws[7], fmaxf(acc1[3], 0.f), s);
+    float s = ws[0] * relu(acc0[0]);
+    s = fmaf(ws[1], relu(acc0[1]), s);
+    s = fmaf(ws[2], relu(acc0[2]), s);
+    s = fmaf(ws[3], relu(acc0[3]), s);
+    s = fmaf(ws[4], relu(acc1[0]), s);
+    s = fmaf(ws[5], relu(acc1[1]), s);
+    s = fmaf(ws[6], relu(acc1[2]), s);
+    s = fmaf(ws[7], relu(acc1[3]), s);
     return s;
 }
 
@@ -83,7 +90,7 @@ __device__ __forceinline__ void load_queries(const uint8_t* __restrict__ q,
 __device__ void fill_neg_inf(float* __restrict__ out_b, int t0, int t1, int N, int s0, int s1) {
     const float ninf = -__builtin_inff();
     for (int t = t0; t < t1; ++t)
-        for (int s = s0 + (int)threadIdx.x; s < s1; s += NT) out_b[(size_t)t * N + s] = ninf;
+        for (int s = s0 + (int)threadIdx.x; s < s1; s += (int)blockDim.x) out_b[(size_t)t * N + s] = ninf;
 }
 
 // ---------------------------------------------------------------------------
@@ -91,13 +98,19 @@ constexpr int TQB = 64;     // queries per workgroup (tiled)
 constexpr int TILE = 64;    // keys per LDS tile
 constexpr int ROWB = 144;   // LDS bytes per key row (128 + 16 pad)
 
+constexpr int OST = 80;     // LDS floats per staged output row (64 + 16: rows 16 banks apart)
+constexpr int NTT = 512;    // threads of the tiled kernel: 8 waves x 8 queries
+constexpr int QPW = TQB / (NTT / 64);   // queries per wave
+constexpr int GPW = QPW / 4;            // 4-query MFMA groups per wave
+
 template <bool FILL>
-__global__ __launch_bounds__(NT) void indexer_fp8_tiled(
+__global__ __launch_bounds__(NTT) void indexer_fp8_tiled(
     const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
     int T, int N, int q_offset, int keys_per_wg) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TILE * ROWB];
     __shared__ float lds_ks[2][TILE];
+    __shared__ __attribute__((aligned(16))) float lds_o[NTT / 64][QPW * OST];
 
     const int b = blockIdx.z;
     const int t0 = blockIdx.x * TQB;
@@ -111,29 +124,30 @@ __global__ __launch_bounds__(NT) void indexer_fp8_tiled(
     float* __restrict__ out_b = scores + row0 * N;
     const uint8_t* __restrict__ k_b = k + (size_t)b * N * DI;
     const float* __restrict__ ks_b = ks + (size_t)b * N;
+    // whole 16-byte output chunks: rows start 16-byte aligned, ranges end on 4
+    const bool vec_out = (N & 3) == 0;
 
     const int n_tiles = s_vis > s_begin ? (s_vis - s_begin + TILE - 1) / TILE : 0;
     if (n_tiles > 0) {
-        const int tw0 = t0 + 16 * wave;
-        i32x8 a[4][2];
-        float ws[4][HI];
+        const int tw0 = t0 + QPW * wave;
+        i32x8 a[GPW][2];
+        float ws[GPW][HI];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) load_queries(q, qs, w, row0, tw0 + 4 * g, T, lane, a[g], ws[g]);
+        for (int g = 0; g < GPW; ++g) load_queries(q, qs, w, row0, tw0 + 4 * g, T, lane, a[g], ws[g]);
+        float* ost = lds_o[wave];
 
-        // cooperative staging: 512 16-byte chunks per tile, two per thread
-        const int c_key0 = tid >> 3, c_key1 = (tid + NT) >> 3, c_piece = tid & 7;
-        uint4 r0, r1;
+        // cooperative staging: 512 16-byte chunks per tile, one per thread
+        const int c_key = tid >> 3, c_piece = tid & 7;
+        uint4 r0;
         float rks = 0.f;
         auto fetch = [&](int s0) {
             const uint4 zero = {0u, 0u, 0u, 0u};
-            const int s_a = s0 + c_key0, s_b = s0 + c_key1;
+            const int s_a = s0 + c_key;
             r0 = s_a < N ? *reinterpret_cast<const uint4*>(k_b + (size_t)s_a * DI + 16 * c_piece) : zero;
-            r1 = s_b < N ? *reinterpret_cast<const uint4*>(k_b + (size_t)s_b * DI + 16 * c_piece) : zero;
             if (tid < TILE) rks = (s0 + tid) < N ? ks_b[s0 + tid] : 0.f;
         };
         auto stage = [&](int buf) {
-            *reinterpret_cast<uint4*>(&lds_k[buf][c_key0 * ROWB + 16 * c_piece]) = r0;
-            *reinterpret_cast<uint4*>(&lds_k[buf][c_key1 * ROWB + 16 * c_piece]) = r1;
+            *reinterpret_cast<uint4*>(&lds_k[buf][c_key * ROWB + 16 * c_piece]) = r0;
             if (tid < TILE) lds_ks[buf][tid] = rks;
         };
 
@@ -146,6 +160,9 @@ __global__ __launch_bounds__(NT) void indexer_fp8_tiled(
             const bool more = it + 1 < n_tiles;
             if (more) fetch(s0 + TILE);
             if (tw0 < t_end) {
+                // a clean tile: every key visible to all of the wave's queries, all in range
+                const bool clean = vec_out && s0 + TILE - 1 <= q_offset + tw0 && tw0 + QPW <= T &&
+                                   s0 + TILE <= s_end;
 #pragma unroll
                 for (int sub = 0; sub < TILE / 16; ++sub) {
                     const int key = 16 * sub + m;
@@ -154,18 +171,39 @@ __global__ __launch_bounds__(NT) void indexer_fp8_tiled(
                                            *reinterpret_cast<const uint4*>(src + 16));
                     const float ksc = lds_ks[buf][key];
                     const int s_abs = s0 + key;
-                    f32x4 acc[4][2];
+                    f32x4 acc[GPW][2];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
+                    for (int g = 0; g < GPW; ++g) {
                         acc[g][0] = mfma_fp8(a[g][0], bf);
                         acc[g][1] = mfma_fp8(a[g][1], bf);
                     }
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int t = tw0 + 4 * g + kb;
+                    for (int g = 0; g < GPW; ++g) {
                         float sc = head_sum(acc[g][0], acc[g][1], ws[g]) * ksc;
-                        if (s_abs > q_offset + t) sc = -__builtin_inff();
-                        if (t < T && s_abs < s_end) out_b[(size_t)t * N + s_abs] = sc;
+                        if (!clean && s_abs > q_offset + tw0 + 4 * g + kb) sc = -__builtin_inff();
+                        ost[(4 * g + kb) * OST + key] = sc;
+                    }
+                }
+                // QPW rows x 64 keys out of LDS: lane l takes 16 bytes of row
+                // 4j + l/16 per step, each row a whole 256-byte segment
+                const int c = lane & 15;
+#pragma unroll
+                for (int j = 0; j < QPW / 4; ++j) {
+                    const int r = 4 * j + (lane >> 4);
+                    const int t = tw0 + r;
+                    const float4 v = *reinterpret_cast<const float4*>(&ost[r * OST + 4 * c]);
+                    float* dst = out_b + (size_t)t * N + s0 + 4 * c;
+                    if (clean) {
+                        *reinterpret_cast<float4*>(dst) = v;
+                    } else if (t < T) {
+                        if (vec_out) {
+                            if (s0 + 4 * c < s_end) *reinterpret_cast<float4*>(dst) = v;
+                        } else {
+                            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (s0 + 4 * c + e < s_end) dst[e] = vv[e];
+                        }
                     }
                 }
             }
@@ -260,10 +298,10 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 const f32x4 acc = mfma_fp8(a[p], bf);
-                float part = ws[p][0] * fmaxf(acc[0], 0.f);
-                part = fmaf(ws[p][1], fmaxf(acc[1], 0.f), part);
-                part = fmaf(ws[p][2], fmaxf(acc[2], 0.f), part);
-                part = fmaf(ws[p][3], fmaxf(acc[3], 0.f), part);
+                float part = ws[p][0] * relu(acc[0]);
+                part = fmaf(ws[p][1], relu(acc[1]), part);
+                part = fmaf(ws[p][2], relu(acc[2]), part);
+                part = fmaf(ws[p][3], relu(acc[3]), part);
                 float v = (part + __shfl_xor(part, 16, 64)) * kss[u];
                 if (s_abs > q_offset + tl[p]) v = -__builtin_inff();
                 sc[p][u] = v;
@@ -356,9 +394,9 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
         kpw = (kpw + TILE - 1) / TILE * TILE;
         dim3 grid(nqb, ceil_div(n_vis, kpw), B);
         if (fill_masked)
-            indexer_fp8_tiled<true><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+            indexer_fp8_tiled<true><<<grid, NTT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
         else
-            indexer_fp8_tiled<false><<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+            indexer_fp8_tiled<false><<<grid, NTT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
         return launch_status();
     }
     const int np = T <= 2 ? 1 : 2;
