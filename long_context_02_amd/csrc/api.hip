@@ -190,10 +190,25 @@ dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* 
     void* attn_w = p;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w, scores, B, T, N, H_I, d_I, q_offset,
-                     idx_dtype, false, s);
-    if (st != DSA_OK) return st;
-    st = launch_topk(scores, idx, B, T, N, k, q_offset, topk_ws, s);
+    if (idx_dtype == DSA_FP8_E4M3FN && indexer_filters(B, T)) {
+        // decode-like batches: candidate lists from a sampled threshold
+        // instead of the score matrix
+        const auto* q8 = static_cast<const uint8_t*>(q_idx);
+        const auto* k8 = static_cast<const uint8_t*>(k_idx);
+        auto* sw = static_cast<uint32_t*>(topk_ws);
+        st = launch_indexer_sample_threshold(q8, q_idx_scale, k8, k_idx_scale, w, sw, B, T, N, q_offset,
+                                             k, s);
+        if (st != DSA_OK) return st;
+        st = launch_indexer_fp8_filtered(q8, q_idx_scale, k8, k_idx_scale, w, sw, B, T, N, q_offset, k, s);
+        if (st != DSA_OK) return st;
+        st = launch_topk_from_candidates(q8, q_idx_scale, k8, k_idx_scale, w, scores, idx, B, T, N, k,
+                                         q_offset, topk_ws, s);
+    } else {
+        st = run_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w, scores, B, T, N, H_I, d_I,
+                         q_offset, idx_dtype, false, s);
+        if (st != DSA_OK) return st;
+        st = launch_topk(scores, idx, B, T, N, k, q_offset, topk_ws, s);
+    }
     if (st != DSA_OK) return st;
     return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, attn_w, s);
 }

@@ -19,6 +19,32 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Workspace carving: every block starts on a 256-byte boundary.
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// ---- top-k selection key and the per-row workspace of few-row selection ----
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 and
+// +0 map to one key, NaN to the lowest.
+__device__ __forceinline__ uint32_t fkey(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0u) return 0x80000000u;
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Batches of at most seg::kMaxRows rows select with several workgroups per
+// row.  Row r owns seg::kRowWords 32-bit words of the top-k workspace: a
+// histogram of the top 12 key bits, four counters (sure picks, candidates,
+// candidate overflow flag, candidate threshold key), the list of sure picks
+// and the candidate list (keys, then token indices).
+namespace seg {
+constexpr int kMaxRows = 255;
+constexpr int kBins = 4096;
+constexpr int kMaxK = 2048;
+constexpr int kCap = 12288;  // candidates per row
+constexpr int kHist = 0, kCtr = kBins, kTheta = kCtr + 3, kDef = kBins + 4, kCKey = kDef + kMaxK,
+              kCIdx = kCKey + kCap;
+constexpr int kRowWords = (kCIdx + kCap + 63) / 64 * 64;
+}  // namespace seg
+inline bool topk_segmented(long long rows) { return rows <= seg::kMaxRows; }
+
 // ---- indexer (indexer.hip) ------------------------------------------------
 // fill_masked: write -inf over the non-causal part of every row (the public
 // entry point promises that); the fused path skips those stores.
@@ -26,6 +52,19 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
                               const float* ks, const float* w, float* scores,
                               int B, int T, int N, int q_offset, bool fill_masked,
                               hipStream_t stream);
+// Decode selection without a score matrix (batches with T < 16 and at most
+// seg::kMaxRows rows): a per-row candidate threshold from a sample of keys,
+// then the stream indexer appending only keys at or above it to the rows'
+// candidate lists in seg_ws (the top-k workspace); scores is not written.
+bool indexer_filters(int B, int T);
+dsa_status launch_indexer_sample_threshold(const uint8_t* q, const float* qs, const uint8_t* k,
+                                           const float* ks, const float* w, uint32_t* seg_ws,
+                                           int B, int T, int N, int q_offset, int top_k,
+                                           hipStream_t stream);
+dsa_status launch_indexer_fp8_filtered(const uint8_t* q, const float* qs, const uint8_t* k,
+                                       const float* ks, const float* w, uint32_t* seg_ws,
+                                       int B, int T, int N, int q_offset, int top_k,
+                                       hipStream_t stream);
 dsa_status launch_indexer_f32(const float* q, const float* k, const float* w, float* scores,
                               int B, int T, int N, int H_I, int d_I, int q_offset,
                               bool fill_masked, hipStream_t stream);
@@ -34,6 +73,14 @@ dsa_status launch_indexer_f32(const float* q, const float* k, const float* w, fl
 size_t topk_workspace_bytes(int B, int T, int N, int k);
 dsa_status launch_topk(const float* scores, int32_t* idx, int B, int T, int N, int k,
                        int q_offset, void* workspace, hipStream_t stream);
+// Selection from the candidate lists the filtered indexer built in the top-k
+// workspace; a row whose list cannot be trusted (fewer than k candidates or
+// an overflow) is rescored into scores (the caller's [B,T,N] buffer) and
+// selected from there.
+dsa_status launch_topk_from_candidates(const uint8_t* q, const float* qs, const uint8_t* k,
+                                       const float* ks, const float* w, float* scores,
+                                       int32_t* idx, int B, int T, int N, int top_k, int q_offset,
+                                       void* workspace, hipStream_t stream);
 
 // ---- sparse attention (attention.hip) ---------------------------------------
 int attn_num_splits(int rows, int k);

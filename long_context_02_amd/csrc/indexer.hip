@@ -21,47 +21,13 @@
 //  * indexer_fp8_stream (T < 16, e.g. decode): the key stream is read once,
 //    so each wave loads its 16-key fragments straight from HBM (see the
 //    kernel for its own MFMA row layout and store pattern).
-#include "dsa_internal.h"
+#include "indexer_math.h"
+#include "topk_select.h"
 
 namespace dsa {
 namespace {
 
-constexpr int HI = 8;      // indexer heads
-constexpr int DI = 128;    // indexer dim = bytes per FP8 row
 constexpr int NT = 256;    // threads per workgroup (4 waves)
-
-// C[16x16] = A[16x128] * B[128x16], FP8 e4m3 both sides, fp32 result.
-// A lane l holds row l%16, B lane l holds column l%16, each as 32 bytes of
-// the 128-byte vector starting at byte 32*(l/16); A and B use the same byte
-// slice, so every q byte meets the matching k byte.  C lane l holds rows
-// 4*(l/16)+i (i = 0..3) of column l%16.
-__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
-}
-
-__device__ __forceinline__ i32x8 pack8(const uint4& x0, const uint4& x1) {
-    return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                 (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-}
-
-// ReLU as one integer max on the bit pattern: negative floats (sign bit
-// set, -0 included) are negative as int32 and become +0, the rest pass
-// unchanged.  (fmaxf would add a NaN-quieting max in front of every use.)
-__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// sum_j ws[j] * ReLU(D_j): acc0 holds heads 0-3, acc1 heads 4-7.
-__device__ __forceinline__ float head_sum(const f32x4& acc0, const f32x4& acc1, const float* ws) {
-    float s = ws[0] * relu(acc0[0]);
-    s = fmaf(ws[1], relu(acc0[1]), s);
-    s = fmaf(ws[2], relu(acc0[2]), s);
-    s = fmaf(ws[3], relu(acc0[3]), s);
-    s = fmaf(ws[4], relu(acc1[0]), s);
-    s = fmaf(ws[5], relu(acc1[1]), s);
-    s = fmaf(ws[6], relu(acc1[2]), s);
-    s = fmaf(ws[7], relu(acc1[3]), s);
-    return s;
-}
 
 // Load the A fragments (one query group of 4 queries, both head halves) and
 // the per-lane head weights w * q_scale of the query whose scores this lane
@@ -228,21 +194,33 @@ constexpr int SU = DSA_STREAM_SU;     // 16-key fragments per wave and block
 static_assert(SU % 4 == 0, "fragments are stored in groups of four");
 
 // Stream kernel.  The 16 MFMA rows are (2 queries x 8 heads), one MFMA per
-// query pair and 16 keys; C lane l holds rows 4*(l/16)+i, i.e. query l/32 of
-// the pair, heads 4*((l/16)&1)+i, and key l%16, so the two head halves of a
-// score meet with one lane exchange (l ^ 16).  NP query pairs per workgroup.
+// query pair and 16 keys (the layout of indexer_math.h).  NP query pairs per
+// workgroup.
 //
 // Each wave walks blocks of 16*SU consecutive keys (the four waves take
 // turns); the scores of 64 consecutive keys are gathered across lanes into
 // one 256-byte store per query.  Key loads are unconditional (addresses
 // clamped into the visible range; values past it are never stored unmasked)
 // and the next block's loads are issued before this block's stores.
-template <bool FILL, int NP>
+//
+// FILTER (the decode selection): instead of storing scores, every causal
+// score whose key is at or above its row's threshold (seg::kTheta, from
+// indexer_sample_threshold) is appended, with its token index, to an LDS
+// list per query row; at the end each list goes to the row's candidate list
+// in the segmented top-k workspace with one global atomic.  A row whose
+// candidates exceed seg::kCap is flagged instead.  Rows with at most k
+// candidates are skipped (their selection is all of them).
+constexpr int FKPW = 1024;            // keys per workgroup when filtering
+
+template <bool FILL, int NP, bool FILTER>
 __global__ __launch_bounds__(NT) void indexer_fp8_stream(
     const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
-    int T, int N, int q_offset, int keys_per_wg) {
+    uint32_t* __restrict__ seg_ws, int T, int N, int q_offset, int keys_per_wg, int top_k) {
     constexpr int SQ = 2 * NP;
+    __shared__ uint32_t c_key[FILTER ? SQ : 1][FILTER ? FKPW : 1];
+    __shared__ int32_t c_idx[FILTER ? SQ : 1][FILTER ? FKPW : 1];
+    __shared__ uint32_t c_cnt[SQ], c_base[SQ];
     const int b = blockIdx.z;
     const int tq0 = blockIdx.y * SQ;
     const int s_begin = blockIdx.x * keys_per_wg;
@@ -256,25 +234,23 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
     const uint8_t* __restrict__ k_b = k + (size_t)b * N * DI;
     const float* __restrict__ ks_b = ks + (size_t)b * N;
 
-    // A rows m: query tq0 + 2p + (m >> 3), head m & 7
     i32x8 a[NP];
     float ws[NP][4];
     int tl[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int ta = tq0 + 2 * p + (m >> 3), h = m & 7;
-        if (ta < T) {
-            const uint4* src = reinterpret_cast<const uint4*>(q + ((row0 + ta) * HI + h) * DI + 32 * kb);
-            a[p] = pack8(src[0], src[1]);
-        } else {
-            a[p] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        tl[p] = tq0 + 2 * p + (kb >> 1);  // the query this lane's C rows belong to
+    for (int p = 0; p < NP; ++p) pair_operands(q, qs, w, row0, tq0 + 2 * p, T, lane, &a[p], ws[p], &tl[p]);
+    // FILTER: per query row of the workgroup, the threshold key (rows that
+    // select everything get ~0u: nothing passes)
+    uint32_t theta[SQ];
+    if (FILTER) {
+        if (tid < SQ) c_cnt[tid] = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h2 = 4 * (kb & 1) + i;
-            ws[p][i] = tl[p] < T ? w[(row0 + tl[p]) * HI + h2] * qs[(row0 + tl[p]) * HI + h2] : 0.f;
+        for (int r = 0; r < SQ; ++r) {
+            const int t = tq0 + r;
+            const bool sel = t < T && (long long)min((long long)N, (long long)q_offset + t + 1) > top_k;
+            theta[r] = sel ? seg_ws[(row0 + t) * seg::kRowWords + seg::kTheta] : ~0u;
         }
+        __syncthreads();
     }
 
     uint4 x0[SU], x1[SU];
@@ -297,12 +273,7 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
             const int s_abs = base + 16 * u + m;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                const f32x4 acc = mfma_fp8(a[p], bf);
-                float part = ws[p][0] * relu(acc[0]);
-                part = fmaf(ws[p][1], relu(acc[1]), part);
-                part = fmaf(ws[p][2], relu(acc[2]), part);
-                part = fmaf(ws[p][3], relu(acc[3]), part);
-                float v = (part + __shfl_xor(part, 16, 64)) * kss[u];
+                float v = pair_score(half_score(mfma_fp8(a[p], bf), ws[p]), kss[u]);
                 if (s_abs > q_offset + tl[p]) v = -__builtin_inff();
                 sc[p][u] = v;
             }
@@ -326,7 +297,25 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
                         const float x = __shfl(sc[p][4 * g + f], 32 * qq + m, 64);
                         v = kb == f ? x : v;
                     }
-                    if (in && tq < t_end) out_b[(size_t)tq * N + key] = v;
+                    if (!FILTER) {
+                        if (in && tq < t_end) out_b[(size_t)tq * N + key] = v;
+                    } else {
+                        const int r = 2 * p + qq;
+                        const uint32_t fk = fkey(v);
+                        const bool pass = in && key <= q_offset + tq && fk >= theta[r];
+                        const uint64_t bal = __ballot(pass);
+                        if (bal) {
+                            uint32_t at = 0;
+                            if (lane == 0) at = atomicAdd(&c_cnt[r], (uint32_t)__popcll(bal));
+                            at = __builtin_amdgcn_readfirstlane(at);
+                            const uint32_t pos = at + __builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                            if (pass) {
+                                c_key[r][pos] = fk;
+                                c_idx[r][pos] = key;
+                            }
+                        }
+                    }
                 }
             }
         }
@@ -343,6 +332,105 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
         const int f0 = s_begin + ((max(s_vis - s_begin, 0) + 15) / 16) * 16;
         if (f0 < s_end) fill_neg_inf(out_b, tq0, t_end, N, f0, s_end);
     }
+    if (FILTER) {
+        __syncthreads();
+        if (tid < t_end - tq0 && c_cnt[tid] > 0u) {
+            uint32_t* wr = seg_ws + (row0 + tq0 + tid) * seg::kRowWords;
+            const uint32_t at = atomicAdd(&wr[seg::kCtr + 1], c_cnt[tid]);
+            if (at + c_cnt[tid] > (uint32_t)seg::kCap) wr[seg::kCtr + 2] = 1u;
+            c_base[tid] = at;
+        }
+        __syncthreads();
+        for (int r = 0; r < t_end - tq0; ++r) {
+            const uint32_t n = c_cnt[r], at = c_base[r];
+            if (n == 0u || at + n > (uint32_t)seg::kCap) continue;
+            uint32_t* wr = seg_ws + (row0 + tq0 + r) * seg::kRowWords;
+            for (int i = tid; i < (int)n; i += NT) {
+                wr[seg::kCKey + at + i] = c_key[r][i];
+                wr[seg::kCIdx + at + i] = (uint32_t)c_idx[r][i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-row threshold for the decode selection.  One 1024-thread workgroup per
+// row with more than k candidates scores S = min(1024, n_cand) keys spread
+// evenly over the row (key floor(i * n_cand / S)), with the stream layout's
+// arithmetic, and takes the key of its r-th largest sample score rounded
+// down to 22 bits, r = mu + 6 sqrt(mu) + 8 with mu = S k / n_cand the
+// expected number of samples among the row's top k.  Keys at or above it
+// hold the row's top k unless the sample is far from typical, and the
+// selection checks that (count >= k) before trusting it.  Also clears the
+// row's candidate counter and overflow flag.
+constexpr int SMP = 1024;
+constexpr int SMT = TT;  // threads (the block helpers of topk_select.h assume TT)
+
+__global__ __launch_bounds__(SMT) void indexer_sample_threshold(
+    const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
+    const float* __restrict__ ks, const float* __restrict__ w, uint32_t* __restrict__ seg_ws,
+    int T, int N, int q_offset, int top_k) {
+    __shared__ uint32_t skey[SMP];
+    __shared__ uint32_t hist[seg::kBins];
+    __shared__ uint32_t sh[SMT / 64 + 1];
+    __shared__ uint32_t res[3];
+    const size_t row = blockIdx.x;
+    const int b = (int)(row / T), t = (int)(row % T);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, kb = lane >> 4;
+    uint32_t* wr = seg_ws + row * seg::kRowWords;
+    const int n_cand = (int)min((long long)N, (long long)q_offset + t + 1);
+    if (tid == 0) {
+        wr[seg::kCtr + 1] = 0u;
+        wr[seg::kCtr + 2] = 0u;
+    }
+    if (n_cand <= top_k) return;
+    const int S = min(SMP, n_cand);
+    const uint8_t* __restrict__ k_b = k + (size_t)b * N * DI;
+    const float* __restrict__ ks_b = ks + (size_t)b * N;
+    i32x8 a;
+    float ws4[4];
+    int tl;
+    pair_operands(q, qs, w, (size_t)b * T, t, t + 1, lane, &a, ws4, &tl);
+    // 16 waves x 4 fragments of 16 samples
+    constexpr int FPW = SMP / 16 / (SMT / 64);
+    uint4 x0[FPW], x1[FPW];
+    float kss[FPW];
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        const int i = 16 * (FPW * wave + f) + m;
+        const int s = (int)(((long long)min(i, S - 1) * n_cand) / S);
+        const uint4* p = reinterpret_cast<const uint4*>(k_b + (size_t)s * DI + 32 * kb);
+        x0[f] = p[0];
+        x1[f] = p[1];
+        kss[f] = ks_b[s];
+    }
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        const float v = pair_score(half_score(mfma_fp8(a, pack8(x0[f], x1[f])), ws4), kss[f]);
+        const int i = 16 * (FPW * wave + f) + m;
+        if (kb == 0 && i < S) skey[i] = fkey(v);
+    }
+    for (int i = tid; i < seg::kBins; i += SMT) hist[i] = 0u;
+    __syncthreads();
+    const float mu = (float)S * (float)top_k / (float)n_cand;
+    const int r = (int)ceilf(mu + 6.f * sqrtf(mu) + 8.f);
+    uint32_t theta = 0u;
+    if (r < S) {
+        for (int i = tid; i < S; i += SMT) atomicAdd(&hist[skey[i] >> 20], 1u);
+        __syncthreads();
+        find_bin(hist, seg::kBins, (uint32_t)r, sh, res);
+        const uint32_t b1 = res[0], r2 = (uint32_t)r - res[1];
+        __syncthreads();
+        for (int i = tid; i < 1024; i += SMT) hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < S; i += SMT)
+            if ((skey[i] >> 20) == b1) atomicAdd(&hist[(skey[i] >> 10) & 1023u], 1u);
+        __syncthreads();
+        find_bin(hist, 1024, r2, sh, res);
+        theta = (b1 << 20) | (res[0] << 10);
+    }
+    if (tid == 0) wr[seg::kTheta] = theta;
 }
 
 // ---------------------------------------------------------------------------
@@ -406,13 +494,43 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
     kpw = (kpw + 64 * SU - 1) / (64 * SU) * (64 * SU);
     dim3 grid(ceil_div(n_vis, kpw), nqg, B);
     auto go = [&](auto kern) {
-        kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+        kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, nullptr, T, N, q_offset, (int)kpw, 0);
     };
     if (np == 1) {
-        if (fill_masked) go(indexer_fp8_stream<true, 1>); else go(indexer_fp8_stream<false, 1>);
+        if (fill_masked) go(indexer_fp8_stream<true, 1, false>); else go(indexer_fp8_stream<false, 1, false>);
     } else {
-        if (fill_masked) go(indexer_fp8_stream<true, 2>); else go(indexer_fp8_stream<false, 2>);
+        if (fill_masked) go(indexer_fp8_stream<true, 2, false>); else go(indexer_fp8_stream<false, 2, false>);
     }
+    return launch_status();
+}
+
+bool indexer_filters(int B, int T) { return T < 16 && topk_segmented((long long)B * T); }
+
+dsa_status launch_indexer_sample_threshold(const uint8_t* q, const float* qs, const uint8_t* k,
+                                           const float* ks, const float* w, uint32_t* seg_ws,
+                                           int B, int T, int N, int q_offset, int top_k,
+                                           hipStream_t stream) {
+    if (!indexer_filters(B, T)) return DSA_ERR_UNSUPPORTED;
+    indexer_sample_threshold<<<dim3((unsigned)(B * T)), SMT, 0, stream>>>(q, qs, k, ks, w, seg_ws, T, N,
+                                                                        q_offset, top_k);
+    return launch_status();
+}
+
+dsa_status launch_indexer_fp8_filtered(const uint8_t* q, const float* qs, const uint8_t* k,
+                                       const float* ks, const float* w, uint32_t* seg_ws,
+                                       int B, int T, int N, int q_offset, int top_k,
+                                       hipStream_t stream) {
+    if (!indexer_filters(B, T)) return DSA_ERR_UNSUPPORTED;
+    const long long n_vis = std::min<long long>(N, (long long)q_offset + T);
+    const int np = T <= 2 ? 1 : 2;
+    const int nqg = ceil_div(T, 2 * np);
+    static_assert(FKPW % (64 * SU) == 0, "filtered key ranges are whole blocks");
+    dim3 grid(ceil_div(n_vis, FKPW), nqg, B);
+    auto go = [&](auto kern) {
+        kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, nullptr, seg_ws, T, N, q_offset, FKPW, top_k);
+    };
+    if (np == 1) go(indexer_fp8_stream<false, 1, true>);
+    else go(indexer_fp8_stream<false, 2, true>);
     return launch_status();
 }
 

@@ -27,299 +27,11 @@
 //
 // Batches of few rows (decode: one row per sequence) instead split every row
 // over several workgroups; see the segmented path below.
-#include "dsa_internal.h"
+#include "indexer_math.h"
+#include "topk_select.h"
 
 namespace dsa {
 namespace {
-
-constexpr int TT = 1024;         // threads per row
-constexpr int NW = TT / 64;      // waves per row
-constexpr int BINS = 4096;       // first digit: key bits 31..20
-constexpr int CAP = 6144;        // LDS candidate capacity
-constexpr int KMAX = 2048;
-
-// Order-preserving map float -> uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t fkey(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) == 0u) return 0x80000000u;                        // -0 == +0
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0u;   // NaN lowest
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t n = __shfl_up(v, o, 64);
-        if (lane >= o) v += n;
-    }
-    return v;
-}
-
-// Exclusive prefix sum of v over the workgroup (thread order); *total gets
-// the sum.  Contains barriers: every thread must call it.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t incl = wave_incl_scan(v);
-    if (lane == 63) sh[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        const uint32_t x = lane < NW ? sh[lane] : 0u;
-        const uint32_t xi = wave_incl_scan(x);
-        if (lane < NW) sh[lane] = xi - x;
-        if (lane == NW - 1) sh[NW] = xi;
-    }
-    __syncthreads();
-    const uint32_t r = sh[wave] + incl - v;
-    *total = sh[NW];
-    __syncthreads();
-    return r;
-}
-
-// Four consecutive scores starting at e (vector load when aligned and whole).
-__device__ __forceinline__ void load4(const float* __restrict__ s, int e, int n, bool vec, float* v) {
-    if (vec && e + 3 < n) {
-        const float4 x = *reinterpret_cast<const float4*>(s + e);
-        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = e + j < n ? s[e + j] : 0.f;
-    }
-}
-
-// Find, over nb histogram bins read in descending bin order, the bin that
-// holds the need-th largest element.  Writes (bin, count above, count in bin)
-// to res.  Every thread must call it; nb <= 4*TT.
-__device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh, uint32_t* res) {
-    const int per = (nb + TT - 1) / TT;      // bins per thread (1 or 4)
-    const int hi = nb - per * (int)threadIdx.x;  // this thread owns bins [hi-per, hi)
-    uint32_t cnt = 0;
-    for (int i = 1; i <= per; ++i)
-        if (hi - i >= 0) cnt += hist[hi - i];
-    uint32_t total;
-    const uint32_t above = block_excl_scan(cnt, sh, &total);
-    if (cnt > 0 && above < need && above + cnt >= need) {
-        uint32_t acc = above;
-        for (int i = 1; i <= per; ++i) {
-            const uint32_t h = hist[hi - i];
-            if (acc + h >= need) {
-                res[0] = (uint32_t)(hi - i);
-                res[1] = acc;
-                res[2] = h;
-                break;
-            }
-            acc += h;
-        }
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t v) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-// LDS of the single-workgroup row selection, carved from one buffer so the
-// segmented path can reuse it as its fallback.
-struct RowLds {
-    uint32_t* hist;   // BINS
-    int32_t* listA;   // KMAX
-    int32_t* listB;   // KMAX
-    uint32_t* ckey;   // CAP
-    int32_t* cidx;    // CAP
-    uint32_t* sh;     // NW + 1
-    uint32_t* res;    // 3
-};
-constexpr int ROW_LDS_WORDS = BINS + 2 * KMAX + 2 * CAP + NW + 1 + 3;
-
-__device__ RowLds carve_row_lds(uint32_t* base) {
-    RowLds L;
-    L.hist = base;
-    L.listA = reinterpret_cast<int32_t*>(L.hist + BINS);
-    L.listB = L.listA + KMAX;
-    L.ckey = reinterpret_cast<uint32_t*>(L.listB + KMAX);
-    L.cidx = reinterpret_cast<int32_t*>(L.ckey + CAP);
-    L.sh = reinterpret_cast<uint32_t*>(L.cidx + CAP);
-    L.res = L.sh + NW + 1;
-    return L;
-}
-
-// Top-k of one row by one 1024-thread workgroup (n_cand > k).
-__device__ void select_row(const float* __restrict__ s, int32_t* __restrict__ out, int n_cand, int k,
-                           const RowLds& L) {
-    uint32_t* hist = L.hist;
-    int32_t* listA = L.listA;
-    int32_t* listB = L.listB;
-    uint32_t* ckey = L.ckey;
-    int32_t* cidx = L.cidx;
-    uint32_t* sh = L.sh;
-    uint32_t* res = L.res;
-    const int tid = threadIdx.x;
-    const uint32_t n = (uint32_t)k;
-    const bool vec = ((reinterpret_cast<uintptr_t>(s) & 15u) == 0);
-
-    // ---- pass 1: histogram of the top 12 key bits
-    for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
-    __syncthreads();
-    for (int base = 0; base < n_cand; base += 4 * TT) {
-        const int e = base + 4 * tid;
-        float v[4];
-        load4(s, e, n_cand, vec, v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (e + j < n_cand) atomicAdd(&hist[fkey(v[j]) >> 20], 1u);
-    }
-    __syncthreads();
-    find_bin(hist, BINS, n, sh, res);
-    const uint32_t b1 = res[0], gt1 = res[1], eq1 = res[2];
-
-    if (eq1 <= (uint32_t)CAP) {
-        // ---- pass 2: ordered compaction into list A (above b1) and C (in b1)
-        uint32_t run_a = 0, run_c = 0;
-        for (int base = 0; base < n_cand; base += 4 * TT) {
-            const int e = base + 4 * tid;
-            float v[4];
-            load4(s, e, n_cand, vec, v);
-            uint32_t key[4], na = 0, nc = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                key[j] = fkey(v[j]);
-                const bool ok = e + j < n_cand;
-                na += (ok && (key[j] >> 20) > b1);
-                nc += (ok && (key[j] >> 20) == b1);
-            }
-            uint32_t tot;
-            const uint32_t ex = block_excl_scan(na | (nc << 16), sh, &tot);
-            uint32_t pa = run_a + (ex & 0xffffu), pc = run_c + (ex >> 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (e + j >= n_cand) continue;
-                const uint32_t d = key[j] >> 20;
-                if (d > b1) {
-                    listA[pa++] = e + j;
-                } else if (d == b1) {
-                    ckey[pc] = key[j];
-                    cidx[pc] = e + j;
-                    ++pc;
-                }
-            }
-            run_a += tot & 0xffffu;
-            run_c += tot >> 16;
-        }
-        __syncthreads();
-
-        // ---- digits 2 and 3 inside C
-        const int nc = (int)eq1;
-        const uint32_t r1 = n - gt1;
-        for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < nc; i += TT) atomicAdd(&hist[(ckey[i] >> 10) & 1023u], 1u);
-        __syncthreads();
-        find_bin(hist, 1024, r1, sh, res);
-        const uint32_t b2 = res[0], gt2 = res[1];
-        const uint32_t r2 = r1 - gt2;
-        for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < nc; i += TT)
-            if (((ckey[i] >> 10) & 1023u) == b2) atomicAdd(&hist[ckey[i] & 1023u], 1u);
-        __syncthreads();
-        find_bin(hist, 1024, r2, sh, res);
-        const uint32_t b3 = res[0], gt3 = res[1];
-        const uint32_t kstar = (b1 << 20) | (b2 << 10) | b3;
-        const uint32_t r3 = r2 - gt3;  // keys == K* to keep, lowest indices first
-
-        // ---- ordered selection from C into list B
-        uint32_t run_g = 0, run_t = 0;
-        for (int base = 0; base < nc; base += TT) {
-            const int i = base + tid;
-            const bool ok = i < nc;
-            const uint32_t key = ok ? ckey[i] : 0u;
-            const uint32_t g = ok && key > kstar, tie = ok && key == kstar;
-            uint32_t tot;
-            const uint32_t ex = block_excl_scan(g | (tie << 16), sh, &tot);
-            const uint32_t tie_before = run_t + (ex >> 16);
-            const uint32_t pos = run_g + (ex & 0xffffu) + min(tie_before, r3);
-            if (g || (tie && tie_before < r3)) listB[pos] = cidx[i];
-            run_g += tot & 0xffffu;
-            run_t += tot >> 16;
-        }
-        __syncthreads();
-
-        // ---- merge the two ascending lists
-        const int na = (int)gt1, nb = (int)r1;
-        for (int i = tid; i < na; i += TT) {
-            const int32_t v = listA[i];
-            out[i + lower_bound(listB, nb, v)] = v;
-        }
-        for (int j = tid; j < nb; j += TT) {
-            const int32_t v = listB[j];
-            out[j + lower_bound(listA, na, v)] = v;
-        }
-        return;
-    }
-
-    // ---- fallback: resolve the remaining digits over HBM, then emit in order
-    uint32_t prefix = b1, need = n - gt1;
-    int shift = 20;
-    while (shift > 0) {
-        const int d = shift >= 10 ? 10 : shift;
-        const uint32_t nbin = 1u << d;
-        for (int i = tid; i < (int)nbin; i += TT) hist[i] = 0u;
-        __syncthreads();
-        for (int base = 0; base < n_cand; base += 4 * TT) {
-            const int e = base + 4 * tid;
-            float v[4];
-            load4(s, e, n_cand, vec, v);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t key = fkey(v[j]);
-                if (e + j < n_cand && (key >> shift) == prefix)
-                    atomicAdd(&hist[(key >> (shift - d)) & (nbin - 1u)], 1u);
-            }
-        }
-        __syncthreads();
-        find_bin(hist, (int)nbin, need, sh, res);
-        need -= res[1];
-        prefix = (prefix << d) | res[0];
-        shift -= d;
-    }
-    const uint32_t kstar = prefix, r = need;
-    uint32_t run_g = 0, run_t = 0;
-    for (int base = 0; base < n_cand; base += 4 * TT) {
-        const int e = base + 4 * tid;
-        float v[4];
-        load4(s, e, n_cand, vec, v);
-        uint32_t key[4], ng = 0, nt = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            key[j] = fkey(v[j]);
-            const bool ok = e + j < n_cand;
-            ng += ok && key[j] > kstar;
-            nt += ok && key[j] == kstar;
-        }
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan(ng | (nt << 16), sh, &tot);
-        uint32_t gb = run_g + (ex & 0xffffu), tb = run_t + (ex >> 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (e + j >= n_cand) continue;
-            if (key[j] > kstar) {
-                out[gb + min(tb, r)] = e + j;
-                ++gb;
-            } else if (key[j] == kstar) {
-                if (tb < r) out[gb + tb] = e + j;
-                ++tb;
-            }
-        }
-        run_g += tot & 0xffffu;
-        run_t += tot >> 16;
-    }
-}
-
 
 __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores,
                                                 int32_t* __restrict__ idx, int T, int N, int k,
@@ -353,11 +65,10 @@ __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores
 //                      path instead
 constexpr int SEG = 16384;              // elements per segment
 constexpr int STT = TT;                 // threads of the segment kernels
-constexpr int CAPG = 12288;             // candidate capacity per row
-constexpr int SEG_MAX_ROWS = 255;       // batches with more rows use topk_rows
+constexpr int CAPG = seg::kCap;         // candidate capacity per row
 // per-row workspace, in 32-bit words
-constexpr int WS_HIST = 0, WS_CTR = BINS, WS_DEF = BINS + 4, WS_CKEY = WS_DEF + KMAX,
-              WS_CIDX = WS_CKEY + CAPG, WS_ROW = (WS_CIDX + CAPG + 63) / 64 * 64;
+constexpr int WS_HIST = seg::kHist, WS_CTR = seg::kCtr, WS_DEF = seg::kDef, WS_CKEY = seg::kCKey,
+              WS_CIDX = seg::kCIdx, WS_ROW = seg::kRowWords;
 // counters: [0] sure picks, [1] candidates, [2] candidate overflow flag
 
 __device__ __forceinline__ int row_candidates(int t, int N, int q_offset) {
@@ -475,7 +186,6 @@ __global__ __launch_bounds__(STT) void topk_seg_collect(const float* __restrict_
     }
 }
 
-constexpr int BM_BITS = BINS * 32;      // index window of one bitmap pass
 constexpr int FIN_LDS_WORDS = 2 * CAPG + BINS + NW + 1 + 3;
 constexpr int K3_LDS_WORDS = FIN_LDS_WORDS > ROW_LDS_WORDS ? FIN_LDS_WORDS : ROW_LDS_WORDS;
 
@@ -523,78 +233,117 @@ __global__ __launch_bounds__(TT) void topk_seg_finalize(const float* __restrict_
     __syncthreads();
     find_bin(hist, 1024, r2, sh, res);
     const uint32_t b3 = res[0], n_tie = res[2];
-    const uint32_t klow = (b2 << 10) | b3;  // low 20 bits of the k-th key
-    const uint32_t r3 = r2 - res[1];        // ties to keep, lowest indices first
-    // when not every tie is kept, the r3-th smallest tie index bounds them:
-    // radix select on ~index (larger = lower index), 12 + 10 + 10 bits
-    uint32_t inv_thr = 0u;  // keep ties with ~index >= inv_thr
-    if (n_tie > r3) {
-        uint32_t prefix = 0u, need = r3;
-        int shift = 32;
-        while (shift > 0) {
-            const int d = shift == 32 ? 12 : 10;
-            const uint32_t nb = 1u << d;
-            for (int i = tid; i < (int)nb; i += TT) hist[i] = 0u;
-            __syncthreads();
-            for (int i = tid; i < n_c; i += TT) {
-                const uint32_t inv = ~(uint32_t)cidx[i];
-                const bool tie = (ckey[i] & 0xFFFFFu) == klow;
-                const bool pre = shift == 32 || (inv >> shift) == prefix;
-                if (tie && pre) atomicAdd(&hist[(inv >> (shift - d)) & (nb - 1u)], 1u);
-            }
-            __syncthreads();
-            find_bin(hist, (int)nb, need, sh, res);
-            need -= res[1];
-            prefix = (prefix << d) | res[0];
-            shift -= d;
-        }
-        inv_thr = prefix;
-    }
-    // ascending output: a bitmap over a window of BM_BITS indices at a time,
-    // one bit per pick, then a scan of the per-thread popcounts
-    uint32_t* bm = hist;
-    uint32_t emitted = 0;
-    for (int w0 = 0; w0 < n_cand; w0 += BM_BITS) {
-        for (int i = tid; i < BINS; i += TT) bm[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n_def; i += TT) {
-            const int e = gdef[i] - w0;
-            if (e >= 0 && e < BM_BITS) atomicOr(&bm[e >> 5], 1u << (e & 31));
-        }
-        for (int i = tid; i < n_c; i += TT) {
-            const uint32_t kl = ckey[i] & 0xFFFFFu;
-            const bool take = kl > klow || (kl == klow && ~(uint32_t)cidx[i] >= inv_thr);
-            const int e = cidx[i] - w0;
-            if (take && e >= 0 && e < BM_BITS) atomicOr(&bm[e >> 5], 1u << (e & 31));
-        }
-        __syncthreads();
-        constexpr int WPT = BINS / TT;  // bitmap words per thread
-        uint32_t m[WPT], cnt = 0;
+    const uint32_t kthr = (ckey[0] & 0xFFF00000u) | (b2 << 10) | b3;  // the k-th key (bin b1 is shared)
+    const uint32_t r3 = r2 - res[1];  // ties to keep, lowest indices first
+    const uint32_t inv_thr = tie_threshold(ckey, cidx, n_c, kthr, n_tie, r3, hist, sh, res);
+    emit_ascending(gdef, n_def, ckey, cidx, n_c, kthr, inv_thr, n_cand, out, hist, sh);
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode selection from candidate lists (built by the filtered indexer from
+// a sampled threshold): one 1024-thread workgroup per row finds the exact
+// k-th key among the row's candidates with the three radix digits, keeps the
+// lowest-index ties and writes the picks in ascending order.  When the list
+// holds fewer than k keys (the threshold was too high) or overflowed, the
+// workgroup rescores the whole row into `scores`, with the stream layout's
+// arithmetic (so the scores are those dsa_indexer_scores returns), and
+// selects from there.
+__device__ void rescore_row(const uint8_t* __restrict__ q, const float* __restrict__ qs,
+                            const uint8_t* __restrict__ kk, const float* __restrict__ ks,
+                            const float* __restrict__ w, float* __restrict__ srow, int b, int t,
+                            int T, int N, int n_cand) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, kb = lane >> 4;
+    const uint8_t* __restrict__ k_b = kk + (size_t)b * N * DI;
+    const float* __restrict__ ks_b = ks + (size_t)b * N;
+    i32x8 a;
+    float ws4[4];
+    int tl;
+    pair_operands(q, qs, w, (size_t)b * T, t, t + 1, lane, &a, ws4, &tl);
+    constexpr int U = 4;  // fragments in flight per wave
+    for (int f0 = 16 * U * wave; f0 < n_cand; f0 += 16 * U * NW) {
+        uint4 x0[U], x1[U];
+        float kss[U];
 #pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-            m[j] = bm[WPT * tid + j];
-            cnt += __popc(m[j]);
+        for (int u = 0; u < U; ++u) {
+            const int s = min(f0 + 16 * u + m, n_cand - 1);
+            const uint4* p = reinterpret_cast<const uint4*>(k_b + (size_t)s * DI + 32 * kb);
+            x0[u] = p[0];
+            x1[u] = p[1];
+            kss[u] = ks_b[s];
         }
-        uint32_t total;
-        uint32_t p = emitted + block_excl_scan(cnt, sh, &total);
 #pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-            uint32_t x = m[j];
-            while (x) {
-                const int b = __ffs(x) - 1;
-                x &= x - 1u;
-                out[p++] = w0 + 32 * (WPT * tid + j) + b;
-            }
+        for (int u = 0; u < U; ++u) {
+            const float v = pair_score(half_score(mfma_fp8(a, pack8(x0[u], x1[u])), ws4), kss[u]);
+            const int s = f0 + 16 * u + m;
+            if (kb == 0 && s < n_cand) srow[s] = v;
         }
-        emitted += total;
     }
+}
+
+__global__ __launch_bounds__(TT) void topk_cand_select(
+    const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ kk,
+    const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
+    const uint32_t* __restrict__ ws, int32_t* __restrict__ idx, int T, int N, int k, int q_offset) {
+    __shared__ uint32_t lds[K3_LDS_WORDS];
+    const int row = blockIdx.x, t = row % T, b = row / T;
+    const int tid = threadIdx.x;
+    const int n_cand = row_candidates(t, N, q_offset);
+    int32_t* __restrict__ out = idx + (size_t)row * k;
+    if (n_cand <= k) {
+        for (int i = tid; i < k; i += TT) out[i] = i < n_cand ? i : -1;
+        return;
+    }
+    const uint32_t* wr = ws + (size_t)row * WS_ROW;
+    const int n_c = (int)wr[WS_CTR + 1];
+    if (wr[WS_CTR + 2] || n_c < k) {
+        float* srow = scores + (size_t)row * N;
+        rescore_row(q, qs, kk, ks, w, srow, b, t, T, N, n_cand);
+        __threadfence();
+        __syncthreads();
+        select_row(srow, out, n_cand, k, carve_row_lds(lds));
+        return;
+    }
+    uint32_t* ckey = lds;                                        // CAPG
+    int32_t* cidx = reinterpret_cast<int32_t*>(ckey + CAPG);     // CAPG
+    uint32_t* hist = reinterpret_cast<uint32_t*>(cidx + CAPG);   // BINS, later the bitmap
+    uint32_t* sh = hist + BINS;                                  // NW + 1
+    uint32_t* res = sh + NW + 1;                                 // 3
+    for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
+    for (int i = tid; i < n_c; i += TT) {
+        ckey[i] = wr[WS_CKEY + i];
+        cidx[i] = (int32_t)wr[WS_CIDX + i];
+    }
+    __syncthreads();
+    // three digits: key bits 31..20, 19..10 and 9..0
+    for (int i = tid; i < n_c; i += TT) atomicAdd(&hist[ckey[i] >> 20], 1u);
+    __syncthreads();
+    find_bin(hist, BINS, (uint32_t)k, sh, res);
+    const uint32_t b1 = res[0], r1 = (uint32_t)k - res[1];
+    for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n_c; i += TT)
+        if ((ckey[i] >> 20) == b1) atomicAdd(&hist[(ckey[i] >> 10) & 1023u], 1u);
+    __syncthreads();
+    find_bin(hist, 1024, r1, sh, res);
+    const uint32_t p2 = (b1 << 10) | res[0], r2 = r1 - res[1];
+    for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n_c; i += TT)
+        if ((ckey[i] >> 10) == p2) atomicAdd(&hist[ckey[i] & 1023u], 1u);
+    __syncthreads();
+    find_bin(hist, 1024, r2, sh, res);
+    const uint32_t kthr = (p2 << 10) | res[0], n_tie = res[2], r3 = r2 - res[1];
+    const uint32_t inv_thr = tie_threshold(ckey, cidx, n_c, kthr, n_tie, r3, hist, sh, res);
+    emit_ascending(nullptr, 0, ckey, cidx, n_c, kthr, inv_thr, n_cand, out, hist, sh);
 }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int T, int, int) {
     const long long rows = (long long)B * T;
-    return rows <= SEG_MAX_ROWS ? (size_t)rows * WS_ROW * sizeof(uint32_t) : 0;
+    return topk_segmented(rows) ? (size_t)rows * WS_ROW * sizeof(uint32_t) : 0;
 }
 
 dsa_status launch_topk(const float* scores, int32_t* idx, int B, int T, int N, int k,
@@ -602,7 +351,7 @@ dsa_status launch_topk(const float* scores, int32_t* idx, int B, int T, int N, i
     if (k > KMAX) return DSA_ERR_UNSUPPORTED;
     if (B > 65535) return DSA_ERR_UNSUPPORTED;
     const long long rows = (long long)B * T;
-    if (rows > SEG_MAX_ROWS) {
+    if (!topk_segmented(rows)) {
         topk_rows<<<dim3(T, B), TT, 0, stream>>>(scores, idx, T, N, k, q_offset);
         return launch_status();
     }
@@ -614,6 +363,16 @@ dsa_status launch_topk(const float* scores, int32_t* idx, int B, int T, int N, i
     topk_seg_hist<<<dim3(nseg, (unsigned)rows), STT, 0, stream>>>(scores, ws, T, N, k, q_offset);
     topk_seg_collect<<<dim3(nseg, (unsigned)rows), STT, 0, stream>>>(scores, ws, T, N, k, q_offset);
     topk_seg_finalize<<<dim3((unsigned)rows), TT, 0, stream>>>(scores, ws, idx, T, N, k, q_offset);
+    return launch_status();
+}
+
+dsa_status launch_topk_from_candidates(const uint8_t* q, const float* qs, const uint8_t* kk,
+                                       const float* ks, const float* w, float* scores,
+                                       int32_t* idx, int B, int T, int N, int top_k, int q_offset,
+                                       void* workspace, hipStream_t stream) {
+    if (top_k > KMAX || !topk_segmented((long long)B * T)) return DSA_ERR_UNSUPPORTED;
+    topk_cand_select<<<dim3((unsigned)(B * T)), TT, 0, stream>>>(
+        q, qs, kk, ks, w, scores, static_cast<const uint32_t*>(workspace), idx, T, N, top_k, q_offset);
     return launch_status();
 }
 

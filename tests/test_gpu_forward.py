@@ -125,6 +125,44 @@ def test_forward_selection_matches_separate_calls(name, B, T):
     torch.cuda.empty_cache()
 
 
+def _forward_vs_separate(wl, g, where):
+    _, _, idx = _forward(wl, g)
+    scores = dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
+                                q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
+    ref = dsa.topk_select(scores, wl.k, wl.q_offset)
+    torch.cuda.synchronize()
+    bad = (idx != ref).any(dim=-1).nonzero()
+    assert bad.numel() == 0, f"{where}: rows {bad[:4].tolist()} differ"
+
+
+def test_decode_selection_fallback_overflow():
+    """Rows whose scores are all equal (zero queries) put every key above the
+    sampled threshold: the candidate list overflows and the row is rescored
+    and selected from the full scores."""
+    dev = gpu_device()
+    wl = WORKLOADS["decode_128k"].with_(B=3)
+    g = make_inputs(wl, seed=9, device=dev)
+    g["q_idx"][1].zero_()
+    print("[forward] decode fallback: overflowing candidate list", flush=True)
+    _forward_vs_separate(wl, g, "overflow")
+
+
+def test_decode_selection_fallback_few_candidates():
+    """Key rows planted exactly at the sampled positions score far above the
+    rest, so the sampled threshold leaves fewer than k candidates: the row
+    must fall back and still select exactly."""
+    dev = gpu_device()
+    wl = WORKLOADS["decode_128k"].with_(B=2, N=8192, q_offset=8191)
+    g = make_inputs(wl, seed=10, device=dev)
+    n_cand, S = 8192, 1024
+    pos = torch.tensor([(i * n_cand) // S for i in range(S)], device=dev)
+    for b in range(wl.B):
+        g["k_idx"][b, pos] = g["q_idx"][b, 0, 0]          # the query's head-0 codes
+        g["k_idx_scale"][b, pos] = g["q_idx_scale"][b, 0, 0] * 4
+    print("[forward] decode fallback: too few candidates", flush=True)
+    _forward_vs_separate(wl, g, "few candidates")
+
+
 def test_deterministic():
     dev = gpu_device()
     wl = WORKLOADS["prefill_8k"].with_(T=2048, N=2048, k=512)
