@@ -13,11 +13,12 @@ line; ``value`` is query tokens per second.  The line also carries the
 roofline position of the step's dominant kernel and the CPU oracle's
 throughput on a bounded sample of the same workload.
 
-Per-kernel times come from a second timed loop that calls the three entry
-points of the path one after the other (indexer scores -> top-k -> sparse
-attention, the kernels dsa_forward runs) with HIP events recorded between
-them on the stream they are launched on, so each kernel runs in the same
-cache state as inside a step.  The measured HBM traffic of the dominant
+Per-part times come from a second timed loop that calls the two entry points
+whose kernels dsa_forward runs (indexer scores + top-k selection, then sparse
+attention) one after the other with HIP events recorded between them on the
+stream they are launched on, so each runs in the cache state it has inside a
+step; a third loop times the standalone score and top-k kernels the same
+way.  The measured HBM traffic of the dominant
 kernel is read from its rocprofv3 counter summary under profiles/ when that
 summary was taken on the current kernel source, else it is null.
 """
@@ -44,7 +45,19 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "attention": "attention.hip"}
+KERNEL_SOURCES = {"select": ("indexer.hip", "topk.hip", "indexer_math.h", "topk_select.h"),
+                  "indexer": ("indexer.hip", "indexer_math.h", "topk_select.h"),
+                  "topk": ("topk.hip", "indexer_math.h", "topk_select.h"),
+                  "attention": ("attention.hip",)}
+
+
+def source_hash(phase):
+    """sha256 over the kernel sources of a phase (in a fixed order)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[phase]:
+        with open(os.path.join(ROOT, "long_context_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -81,6 +94,13 @@ def work(wl):
             "flop_unit": "fp8" if fp8 else "f32",
         },
         "topk": {"flops": 0, "bytes": idx_pairs * 4 + wl.B * wl.T * wl.k * 4, "flop_unit": None},
+        # scores and selection as one step: the indexer's inputs in, the
+        # selected indices out (the scores are an intermediate)
+        "select": {
+            "flops": idx_pairs * 2 * wl.H_I * wl.d_I,
+            "bytes": keys_read * key_bytes + wl.B * wl.T * qrow_bytes + wl.B * wl.T * wl.k * 4,
+            "flop_unit": "fp8" if fp8 else "f32",
+        },
         "attention": {
             "flops": attn_pairs * 2 * wl.H * (wl.d_qk + wl.d_v),
             "bytes": gathered_rows * kv_row + wl.B * wl.T * (wl.H * (wl.d_qk + wl.d_v) * el + wl.k * 4),
@@ -114,9 +134,8 @@ def roofline(phase, w, seconds):
 def measured_traffic(phase, wl):
     """HBM bytes per launch of `phase` on `wl` from the counter summary in
     profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy calibration),
-    or None when there is none or it was taken on another kernel source."""
+    or None when there is none or it was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"{phase}_{wl.name}_traffic.txt")
-    src = os.path.join(ROOT, "long_context_02_amd", "csrc", KERNEL_SOURCES[phase])
     if not os.path.exists(path):
         return None
     fields = {}
@@ -125,9 +144,7 @@ def measured_traffic(phase, wl):
             if "=" in ln and not ln.startswith("#"):
                 key, val = ln.split("=", 1)
                 fields[key.strip()] = val.strip()
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha or "hbm_bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha256") != source_hash(phase) or "hbm_bytes_per_launch" not in fields:
         return None
     return int(fields["hbm_bytes_per_launch"])
 
@@ -158,6 +175,25 @@ def timed(fn, steps, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def timed_sequence(parts, steps, warmup, stream):
+    """Average milliseconds of each callable when all are called in sequence,
+    `steps` times, with HIP events recorded between them on `stream`."""
+    names = list(parts)
+    for _ in range(warmup):
+        for fn in parts.values():
+            fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, name in enumerate(names):
+            parts[name]()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+            for j, name in enumerate(names)}
 
 
 def cpu_baseline(wl, g, budget_s):
@@ -248,42 +284,43 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     ms = timed(step, args.steps, stream)
 
-    # the three kernels of a step: the entry points called in sequence, HIP
-    # events between them on the launch stream
+    # the step's two parts, as dsa_forward runs them (scores + selection,
+    # then attention), called in sequence through their entry points with
+    # HIP events between them on the launch stream; then the standalone
+    # score and top-k kernels the same way
     scores = torch.empty(B, T, N, dtype=torch.float32, device=dev)
     idx = torch.empty(B, T, wl.k, dtype=torch.int32, device=dev)
     attn_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_ATTN, B, T, N, wl.H, wl.d_v, wl.k)),
                           dtype=torch.uint8, device=dev)
+    sel_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_SELECT, B, T, N, 1, 1, wl.k)),
+                         dtype=torch.uint8, device=dev)
     topk_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_TOPK, B, T, N, 1, 1, wl.k)),
                           dtype=torch.uint8, device=dev)
-    phases = {
+    step_parts = {
+        "select": lambda: dsa.indexer_select(g["q_idx"], g["k_idx"], g["w"], wl.k, wl.q_offset,
+                                             q_idx_scale=g["q_idx_scale"],
+                                             k_idx_scale=g["k_idx_scale"], out=idx, workspace=sel_ws),
+        "attention": lambda: dsa.sparse_mla_attn(g["q"], g["kv"], idx, wl.d_v, wl.sm_scale,
+                                                 out=out, lse=False, workspace=attn_ws),
+    }
+    components = {
         "indexer": lambda: dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
                                               q_idx_scale=g["q_idx_scale"],
                                               k_idx_scale=g["k_idx_scale"], out=scores),
         "topk": lambda: dsa.topk_select(scores, wl.k, wl.q_offset, out=idx, workspace=topk_ws),
-        "attention": lambda: dsa.sparse_mla_attn(g["q"], g["kv"], idx, wl.d_v, wl.sm_scale,
-                                                 out=out, lse=False, workspace=attn_ws),
     }
-    names = list(phases)
-    for _ in range(args.warmup):
-        for fn in phases.values():
-            fn()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        for j, name in enumerate(names):
-            phases[name]()
-            ev[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    phase_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-                for j, name in enumerate(names)}
+    phase_ms = timed_sequence(step_parts, args.steps, args.warmup, stream)
+    comp_ms = timed_sequence(components, args.steps, args.warmup, stream)
     w = work(wl)
     dom = max(phase_ms, key=phase_ms.get)
     roof = roofline(dom, w[dom], phase_ms[dom] / 1e3)
     roof["traffic"] = measured_traffic(dom, wl)
-    t_roof = sum(phase_floor(w[p]) for p in w)
+    t_roof = sum(phase_floor(w[p]) for p in ("indexer", "topk", "attention"))
+    per_kernel = {}
+    for name, t_ms in {**phase_ms, **comp_ms}.items():
+        r = roofline(name, w[name], t_ms / 1e3)
+        per_kernel[name] = {"ms": round(t_ms, 4), "bound": r["bound"], "achieved": r["achieved"],
+                            "unit": r["unit"], "frac": r["frac"]}
 
     line = {
         "metric": "DSA tokens/s (indexer+top-k+sparse attn) at 128K ctx; % of MFMA / HBM roofline",
@@ -304,6 +341,7 @@ def main():
                    "parallelism": "single GPU"},
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "roofline": roof,
+        "kernels": per_kernel,
         # the whole step against the sum of the phases' floors at published peaks
         "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 4),
                           "frac": round(t_roof / (ms / 1e3), 4)},

@@ -69,7 +69,8 @@ typedef enum dsa_dtype {
 typedef enum dsa_op {
     DSA_OP_TOPK = 0,
     DSA_OP_ATTN = 1,
-    DSA_OP_FORWARD = 2
+    DSA_OP_FORWARD = 2,
+    DSA_OP_SELECT = 3
 } dsa_op;
 
 /*
@@ -149,11 +150,36 @@ DSA_API dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int3
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Index scores and top-k selection in one call: idx as dsa_topk_select would
+ * return it for the scores dsa_indexer_scores computes (same arguments,
+ * same ranking and tie rule), without handing the score matrix to the
+ * caller ("Paper Breakdown: DeepSeek-V3.2", section 2: the indexer's scores
+ * serve only to pick Top-k(I[t,:])).
+ *
+ *  idx [B,T,k] int32 output, ascending indices then -1 padding
+ * For FP8 batches with T < 16 and at most 255 rows (decode) the scores are
+ * never materialised: a per-row threshold taken from a sample of 1024 keys
+ * filters the keys into a candidate list and the exact selection is made
+ * among the candidates; a row whose list holds fewer than k keys or
+ * overflows is rescored in full and selected from that, so the result is
+ * always the exact one.  Other shapes compute the scores and select.  The
+ * workspace (dsa_workspace_size(DSA_OP_SELECT, ...) bytes, 16-byte aligned)
+ * holds the score matrix and the selection lists.
+ */
+DSA_API dsa_status dsa_indexer_select(const void* q_idx, const float* q_idx_scale,
+                              const void* k_idx, const float* k_idx_scale,
+                              const float* w, int32_t* idx,
+                              int B, int T, int N, int H_I, int d_I, int k, int q_offset,
+                              dsa_dtype idx_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The whole DSA path: indexer scores -> top-k selection -> sparse attention,
  * for prefill, decode and chunked prefill alike (see q_offset above).
- * Arguments are those of the three calls above; idx_out [B,T,k] receives the
- * selected indices when non-NULL.  The workspace holds the score matrix and
- * the other intermediates: size it with dsa_workspace_size(DSA_OP_FORWARD).
+ * Arguments are those of the calls above; idx_out [B,T,k] receives the
+ * selected indices when non-NULL.  The selection is dsa_indexer_select's.
+ * The workspace holds the score matrix and the other intermediates: size it
+ * with dsa_workspace_size(DSA_OP_FORWARD).
  */
 DSA_API dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale,
                        const void* k_idx, const float* k_idx_scale,

@@ -26,13 +26,13 @@ import torch
 
 __all__ = [
     "DSAError", "lib", "lib_path", "indexer_scores", "topk_select", "sparse_mla_attn",
-    "forward", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD",
+    "forward", "indexer_select", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD", "OP_SELECT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-OP_TOPK, OP_ATTN, OP_FORWARD = 0, 1, 2
+OP_TOPK, OP_ATTN, OP_FORWARD, OP_SELECT = 0, 1, 2, 3
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_forward.argtypes = [vp, fp, vp, fp, fp, vp, vp, vp, fp, i32p,
                               ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, sz, vp]
     L.dsa_forward.restype = ci
+    L.dsa_indexer_select.argtypes = [vp, fp, vp, fp, fp, i32p, ci, ci, ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.dsa_indexer_select.restype = ci
     L.dsa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     L.dsa_workspace_size.restype = sz
     L.dsa_status_string.argtypes = [ci]
@@ -184,6 +186,26 @@ def indexer_scores(q_idx, k_idx, w, q_offset: int, q_idx_scale=None, k_idx_scale
         st = lib().dsa_indexer_scores(_ptr(q_idx), _ptr(q_idx_scale), _ptr(k_idx), _ptr(k_idx_scale),
                                       _ptr(w), _ptr(out), B, T, N, H_I, d_I, q_offset, dt, _stream(dev))
     _raise("dsa_indexer_scores", st)
+    return out
+
+
+def indexer_select(q_idx, k_idx, w, k: int, q_offset: int, q_idx_scale=None, k_idx_scale=None,
+                   out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores and top-k selection in one call: int32 [B,T,k] ascending
+    token indices, -1 padded (the scores are not returned)."""
+    dt, q_idx, k_idx, (B, T, N, H_I, d_I) = _indexer_args(q_idx, k_idx, w, q_idx_scale, k_idx_scale)
+    dev = q_idx.device
+    if out is None:
+        out = torch.empty(B, T, k, dtype=torch.int32, device=dev)
+    _check("out", out, torch.int32, (B, T, k), dev)
+    need = workspace_size(OP_SELECT, B, T, N, 1, 1, k) if 1 <= k <= 2048 else 0
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = lib().dsa_indexer_select(_ptr(q_idx), _ptr(q_idx_scale), _ptr(k_idx), _ptr(k_idx_scale),
+                                      _ptr(w), _ptr(out), B, T, N, H_I, d_I, k, q_offset, dt, _ptr(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(dev))
+    _raise("dsa_indexer_select", st)
     return out
 
 

@@ -85,6 +85,38 @@ dsa_status run_indexer(const void* q_idx, const float* q_scale, const void* k_id
                               w, scores, B, T, N, H_I, d_I, q_offset, fill, s);
 }
 
+// Workspace of the selection: the [B,T,N] fp32 scores, then the top-k
+// workspace (per-row lists for batches of few rows).
+size_t select_ws(int B, int T, int N, int k) {
+    return align_up((size_t)B * T * N * sizeof(float)) + topk_workspace_bytes(B, T, N, k);
+}
+
+dsa_status run_select(const void* q_idx, const float* q_scale, const void* k_idx,
+                      const float* k_scale, const float* w, int32_t* idx, int B, int T, int N,
+                      int H_I, int d_I, int k, int q_offset, dsa_dtype dt, void* workspace,
+                      hipStream_t s) {
+    float* scores = static_cast<float*>(workspace);
+    void* topk_ws = static_cast<char*>(workspace) + align_up((size_t)B * T * N * sizeof(float));
+    if (dt == DSA_FP8_E4M3FN && indexer_filters(B, T)) {
+        // decode-like batches: candidate lists from a sampled threshold
+        // instead of the score matrix
+        const auto* q8 = static_cast<const uint8_t*>(q_idx);
+        const auto* k8 = static_cast<const uint8_t*>(k_idx);
+        auto* sw = static_cast<uint32_t*>(topk_ws);
+        dsa_status st = launch_indexer_sample_threshold(q8, q_scale, k8, k_scale, w, sw, B, T, N,
+                                                        q_offset, k, s);
+        if (st != DSA_OK) return st;
+        st = launch_indexer_fp8_filtered(q8, q_scale, k8, k_scale, w, sw, B, T, N, q_offset, k, s);
+        if (st != DSA_OK) return st;
+        return launch_topk_from_candidates(q8, q_scale, k8, k_scale, w, scores, idx, B, T, N, k,
+                                           q_offset, topk_ws, s);
+    }
+    dsa_status st = run_indexer(q_idx, q_scale, k_idx, k_scale, w, scores, B, T, N, H_I, d_I,
+                                q_offset, dt, false, s);
+    if (st != DSA_OK) return st;
+    return launch_topk(scores, idx, B, T, N, k, q_offset, topk_ws, s);
+}
+
 dsa_status run_attn(const void* q, const void* kv, const int32_t* idx, void* out, float* lse,
                     int B, int T, int N, int H, int d_qk, int d_v, int k, float sm_scale,
                     dsa_dtype dt, void* ws, hipStream_t s) {
@@ -116,10 +148,10 @@ size_t dsa_workspace_size(int op, int B, int T, int N, int H, int d_v, int k) {
     switch (op) {
         case DSA_OP_TOPK: return topk_workspace_bytes(B, T, N, k);
         case DSA_OP_ATTN: return attn_ws(B, T, H, d_v, k);
+        case DSA_OP_SELECT: return select_ws(B, T, N, k);
         case DSA_OP_FORWARD:
-            return align_up((size_t)B * T * N * sizeof(float)) +
-                   align_up((size_t)B * T * k * sizeof(int32_t)) +
-                   align_up(topk_workspace_bytes(B, T, N, k)) + attn_ws(B, T, H, d_v, k);
+            return align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t)) +
+                   attn_ws(B, T, H, d_v, k);
         default: return (size_t)-1;
     }
 }
@@ -146,6 +178,24 @@ dsa_status dsa_topk_select(const float* scores, int32_t* idx, int B, int T, int 
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     return launch_topk(scores, idx, B, T, N, k, q_offset, workspace,
                        static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_indexer_select(const void* q_idx, const float* q_idx_scale, const void* k_idx,
+                              const float* k_idx_scale, const float* w, int32_t* idx, int B, int T,
+                              int N, int H_I, int d_I, int k, int q_offset, dsa_dtype idx_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    // the scores go to the workspace, so pass a stand-in for the check
+    dsa_status st = check_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w,
+                                  reinterpret_cast<const float*>(16), B, T, N, H_I, d_I, q_offset,
+                                  idx_dtype);
+    if (st != DSA_OK) return st;
+    if (!idx || !aligned16(idx)) return DSA_ERR_INVALID_ARG;
+    if (k < 1) return DSA_ERR_INVALID_ARG;
+    if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+    const size_t need = select_ws(B, T, N, k);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
+    return run_select(q_idx, q_idx_scale, k_idx, k_idx_scale, w, idx, B, T, N, H_I, d_I, k, q_offset,
+                      idx_dtype, workspace, static_cast<hipStream_t>(stream));
 }
 
 dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx, void* out,
@@ -181,34 +231,12 @@ dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* 
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
 
     char* p = static_cast<char*>(workspace);
-    float* scores = reinterpret_cast<float*>(p);
-    p += align_up((size_t)B * T * N * sizeof(float));
-    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p);
-    p += align_up((size_t)B * T * k * sizeof(int32_t));
-    void* topk_ws = p;
-    p += align_up(topk_workspace_bytes(B, T, N, k));
-    void* attn_w = p;
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p + align_up(select_ws(B, T, N, k)));
+    void* attn_w = p + align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t));
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (idx_dtype == DSA_FP8_E4M3FN && indexer_filters(B, T)) {
-        // decode-like batches: candidate lists from a sampled threshold
-        // instead of the score matrix
-        const auto* q8 = static_cast<const uint8_t*>(q_idx);
-        const auto* k8 = static_cast<const uint8_t*>(k_idx);
-        auto* sw = static_cast<uint32_t*>(topk_ws);
-        st = launch_indexer_sample_threshold(q8, q_idx_scale, k8, k_idx_scale, w, sw, B, T, N, q_offset,
-                                             k, s);
-        if (st != DSA_OK) return st;
-        st = launch_indexer_fp8_filtered(q8, q_idx_scale, k8, k_idx_scale, w, sw, B, T, N, q_offset, k, s);
-        if (st != DSA_OK) return st;
-        st = launch_topk_from_candidates(q8, q_idx_scale, k8, k_idx_scale, w, scores, idx, B, T, N, k,
-                                         q_offset, topk_ws, s);
-    } else {
-        st = run_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w, scores, B, T, N, H_I, d_I,
-                         q_offset, idx_dtype, false, s);
-        if (st != DSA_OK) return st;
-        st = launch_topk(scores, idx, B, T, N, k, q_offset, topk_ws, s);
-    }
+    st = run_select(q_idx, q_idx_scale, k_idx, k_idx_scale, w, idx, B, T, N, H_I, d_I, k, q_offset,
+                    idx_dtype, workspace, s);
     if (st != DSA_OK) return st;
     return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, attn_w, s);
 }

@@ -54,6 +54,10 @@ def test_workspace_sizes():
     # prefill-sized batches need no split workspace; f32 shapes never do
     assert dsa.workspace_size(dsa.OP_ATTN, 1, 8192, 8192, 128, 512, 2048) == 0
     assert dsa.workspace_size(dsa.OP_ATTN, 1, 4, 256, 16, 64, 64) == 0
+    # the fused selection holds the scores and, for few rows, the row lists
+    sel = dsa.workspace_size(dsa.OP_SELECT, 64, 1, 131072, 1, 1, 2048)
+    assert sel >= 64 * 131072 * 4 + seg
+    assert dsa.workspace_size(dsa.OP_SELECT, 1, 4096, 131072, 1, 1, 2048) >= 4096 * 131072 * 4
     with pytest.raises(ValueError):
         dsa.workspace_size(dsa.OP_FORWARD, 1, 1, 1, 128, 512, 4096)
     with pytest.raises(ValueError):
@@ -109,6 +113,21 @@ def test_attention_rejects_bad_arguments():
     assert call(scale=float("nan")) == 1
     assert call(dt=dsa.FP8_E4M3FN) == 2
     assert call(H=16, dqk=80, dv=96, dt=dsa.F32) == 2     # d_v > d_qk
+
+
+def test_indexer_select_rejects_bad_arguments():
+    f = dsa.lib().dsa_indexer_select
+
+    def call(ptrs=None, k=4, ws=P, wsb=1 << 20, q_offset=4, dt=dsa.FP8_E4M3FN):
+        ptrs = ptrs or [P, P, P, P, P, P]
+        return f(*ptrs, 1, 4, 8, 8, 128, k, q_offset, dt, ws, wsb, None)
+
+    assert call(ptrs=[P, P, P, P, P, None]) == 1          # no idx
+    assert call(ptrs=[None, P, P, P, P, P]) == 1
+    assert call(k=0) == 1 and call(k=4096) == 2
+    assert call(q_offset=5) == 1
+    assert call(ws=None) == 3 and call(wsb=16) == 3
+    assert call(dt=dsa.BF16) == 2
 
 
 def test_forward_rejects_small_workspace():

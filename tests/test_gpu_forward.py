@@ -106,33 +106,34 @@ def test_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("name,B,T", [("decode_128k", 64, 1), ("decode_128k", 4, 2),
-                                      ("chunk_128k", 2, 7)])
+                                      ("chunk_128k", 2, 7), ("prefill_8k", 1, 300)])
 def test_forward_selection_matches_separate_calls(name, B, T):
-    """dsa_forward's selection equals, bit for bit, dsa_topk_select run on
-    dsa_indexer_scores' output: the same score kernel (without the -inf fill
-    of the non-causal part) and the same selection over the workspace."""
+    """The selection inside dsa_forward (and dsa_indexer_select) equals, bit
+    for bit, dsa_topk_select run on dsa_indexer_scores' output: candidate
+    lists from a sampled threshold for few-row FP8 batches, the score matrix
+    otherwise."""
     dev = gpu_device()
     wl = WORKLOADS[name].with_(B=B, T=T, q_offset=WORKLOADS[name].N - T)
     print(f"[forward] vs separate calls {name} B={B} T={T}", flush=True)
     g = make_inputs(wl, seed=5, device=dev)
-    _, _, idx = _forward(wl, g)
-    scores = dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
-                                q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
-    ref = dsa.topk_select(scores, wl.k, wl.q_offset)
-    torch.cuda.synchronize()
-    assert torch.equal(idx, ref)
-    del g, scores
+    _forward_vs_separate(wl, g, f"{name} B={B} T={T}")
+    del g
     torch.cuda.empty_cache()
 
 
 def _forward_vs_separate(wl, g, where):
+    """dsa_forward's and dsa_indexer_select's selections both equal
+    dsa_topk_select on dsa_indexer_scores' output, bit for bit."""
     _, _, idx = _forward(wl, g)
+    sel = dsa.indexer_select(g["q_idx"], g["k_idx"], g["w"], wl.k, wl.q_offset,
+                             q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
     scores = dsa.indexer_scores(g["q_idx"], g["k_idx"], g["w"], wl.q_offset,
                                 q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
     ref = dsa.topk_select(scores, wl.k, wl.q_offset)
     torch.cuda.synchronize()
-    bad = (idx != ref).any(dim=-1).nonzero()
-    assert bad.numel() == 0, f"{where}: rows {bad[:4].tolist()} differ"
+    for name, got in (("dsa_forward", idx), ("dsa_indexer_select", sel)):
+        bad = (got != ref).any(dim=-1).nonzero()
+        assert bad.numel() == 0, f"{where}: {name} rows {bad[:4].tolist()} differ"
 
 
 def test_decode_selection_fallback_overflow():
