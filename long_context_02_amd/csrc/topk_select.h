@@ -14,7 +14,7 @@ namespace {
 constexpr int TT = 1024;         // threads per row
 constexpr int NW = TT / 64;      // waves per row
 constexpr int BINS = seg::kBins; // first digit: key bits 31..20
-constexpr int CAP = 6144;        // LDS candidate capacity
+constexpr int CAP = 4096;        // LDS candidate capacity (two workgroups per CU)
 constexpr int KMAX = seg::kMaxK;
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
