@@ -411,25 +411,8 @@ __global__ __launch_bounds__(SMT) void indexer_sample_threshold(
         const int i = 16 * (FPW * wave + f) + m;
         if (kb == 0 && i < S) skey[i] = fkey(v);
     }
-    for (int i = tid; i < seg::kBins; i += SMT) hist[i] = 0u;
     __syncthreads();
-    const float mu = (float)S * (float)top_k / (float)n_cand;
-    const int r = (int)ceilf(mu + 6.f * sqrtf(mu) + 8.f);
-    uint32_t theta = 0u;
-    if (r < S) {
-        for (int i = tid; i < S; i += SMT) atomicAdd(&hist[skey[i] >> 20], 1u);
-        __syncthreads();
-        find_bin(hist, seg::kBins, (uint32_t)r, sh, res);
-        const uint32_t b1 = res[0], r2 = (uint32_t)r - res[1];
-        __syncthreads();
-        for (int i = tid; i < 1024; i += SMT) hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < S; i += SMT)
-            if ((skey[i] >> 20) == b1) atomicAdd(&hist[(skey[i] >> 10) & 1023u], 1u);
-        __syncthreads();
-        find_bin(hist, 1024, r2, sh, res);
-        theta = (b1 << 20) | (res[0] << 10);
-    }
+    const uint32_t theta = sample_threshold(skey, S, top_k, n_cand, 6.f, 8.f, hist, sh, res);
     if (tid == 0) wr[seg::kTheta] = theta;
 }
 

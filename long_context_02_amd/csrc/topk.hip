@@ -33,19 +33,98 @@
 namespace dsa {
 namespace {
 
+// One pass per row.  A threshold from a sample of the row (128 blocks of 16
+// consecutive scores spread over it) filters the keys while the row is read
+// once; each wave appends the keys at or above it to its own LDS region
+// (positions from a ballot, no atomics), the waves taking interleaved 64-key
+// blocks so that a dense stretch of high scores spreads over all of them.
+// The exact top-k is then selected among the candidates (all CAP1 slots; the
+// unused ones hold key 0).  A row whose sample
+// misleads (fewer than k candidates, or a wave region full) and short rows
+// take the two-pass selection instead.
+constexpr int SAMP_BLOCKS = 128, SAMP_BLK = 16, SAMP = SAMP_BLOCKS * SAMP_BLK;
+constexpr int WREG = 384;              // candidate slots per wave
+constexpr int CAP1 = WREG * NW;        // 6144
+constexpr int ONEPASS_LDS_WORDS = 2 * CAP1 + BINS + NW + 1 + 3 + NW + 1;
+constexpr int ROWS_LDS_WORDS = ONEPASS_LDS_WORDS > ROW_LDS_WORDS ? ONEPASS_LDS_WORDS : ROW_LDS_WORDS;
+
 __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores,
                                                 int32_t* __restrict__ idx, int T, int N, int k,
                                                 int q_offset) {
-    __shared__ uint32_t lds[ROW_LDS_WORDS];
+    __shared__ uint32_t lds[ROWS_LDS_WORDS];
     const int t = blockIdx.x, b = blockIdx.y;
     const size_t row = (size_t)b * T + t;
     const int n_cand = (int)min((long long)N, (long long)q_offset + t + 1);
     int32_t* __restrict__ out = idx + row * k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (n_cand <= k) {  // every candidate is kept
-        for (int i = threadIdx.x; i < k; i += TT) out[i] = i < n_cand ? i : -1;
+        for (int i = tid; i < k; i += TT) out[i] = i < n_cand ? i : -1;
         return;
     }
-    select_row(scores + row * N, out, n_cand, k, carve_row_lds(lds));
+    const float* __restrict__ s = scores + row * N;
+    if (n_cand < 16 * SAMP) {  // shorter rows: the two-pass selection is faster
+        select_row(s, out, n_cand, k, carve_row_lds(lds));
+        return;
+    }
+    uint32_t* ckey = lds;                                        // CAP1 (first the sample)
+    int32_t* cidx = reinterpret_cast<int32_t*>(lds + CAP1);      // CAP1
+    uint32_t* hist = lds + 2 * CAP1;                             // BINS
+    uint32_t* sh = hist + BINS;                                  // NW + 1
+    uint32_t* res = sh + NW + 1;                                 // 3
+    uint32_t* wcnt = res + 3;                                    // NW + 1
+    // sample: block j starts at j * (n_cand - 16) / 127; 8 threads x 2 keys per block
+    {
+        const int j = tid >> 3, o = 2 * (tid & 7);
+        const int st = (int)(((long long)j * (n_cand - SAMP_BLK)) / (SAMP_BLOCKS - 1));
+        ckey[SAMP_BLK * j + o] = fkey(s[st + o]);
+        ckey[SAMP_BLK * j + o + 1] = fkey(s[st + o + 1]);
+    }
+    __syncthreads();
+    const uint32_t theta = sample_threshold(ckey, SAMP, k, n_cand, 4.f, 4.f, hist, sh, res);
+    // one pass: lane l of wave w reads 4 scores of 64-key block 16*(l/16) + w
+    // of each 4096-key stretch, at offset 4*(l%16)
+    const bool vec = ((reinterpret_cast<uintptr_t>(s) & 15u) == 0);
+    uint32_t* wkey = ckey + WREG * wave;
+    int32_t* widx = cidx + WREG * wave;
+    uint32_t fill = 0;  // wave-uniform
+    for (int base = 0; base < n_cand; base += 4 * TT) {
+        const int e = base + 64 * (16 * (lane >> 4) + wave) + 4 * (lane & 15);
+        float v[4];
+        load4(s, e, n_cand, vec, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t key = fkey(v[j]);
+            const bool pass = e + j < n_cand && key >= theta;
+            const uint64_t bal = __ballot(pass);
+            const uint32_t c = (uint32_t)__popcll(bal);
+            if (c == 0u) continue;
+            const uint32_t pos = fill + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (pass && pos < (uint32_t)WREG) {
+                wkey[pos] = key;
+                widx[pos] = e + j;
+            }
+            fill += c;
+        }
+    }
+    // the wave's unused slots get key 0, below the (positive) threshold: never
+    // picked, never tied with the k-th key
+    for (int i = (int)fill + lane; i < WREG; i += 64) wkey[i] = 0u;
+    if (lane == 0) wcnt[wave] = fill;
+    __syncthreads();
+    uint32_t n_c = 0;
+    bool over = false;
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t c = wcnt[w];
+        over |= c > (uint32_t)WREG;
+        n_c += c;
+    }
+    if (over || n_c < (uint32_t)k) {
+        __syncthreads();
+        select_row(s, out, n_cand, k, carve_row_lds(lds));
+        return;
+    }
+    select_candidates(ckey, cidx, CAP1, k, n_cand, out, hist, sh, res);
 }
 
 // ---------------------------------------------------------------------------
@@ -310,33 +389,12 @@ __global__ __launch_bounds__(TT) void topk_cand_select(
     uint32_t* hist = reinterpret_cast<uint32_t*>(cidx + CAPG);   // BINS, later the bitmap
     uint32_t* sh = hist + BINS;                                  // NW + 1
     uint32_t* res = sh + NW + 1;                                 // 3
-    for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
     for (int i = tid; i < n_c; i += TT) {
         ckey[i] = wr[WS_CKEY + i];
         cidx[i] = (int32_t)wr[WS_CIDX + i];
     }
     __syncthreads();
-    // three digits: key bits 31..20, 19..10 and 9..0
-    for (int i = tid; i < n_c; i += TT) atomicAdd(&hist[ckey[i] >> 20], 1u);
-    __syncthreads();
-    find_bin(hist, BINS, (uint32_t)k, sh, res);
-    const uint32_t b1 = res[0], r1 = (uint32_t)k - res[1];
-    for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n_c; i += TT)
-        if ((ckey[i] >> 20) == b1) atomicAdd(&hist[(ckey[i] >> 10) & 1023u], 1u);
-    __syncthreads();
-    find_bin(hist, 1024, r1, sh, res);
-    const uint32_t p2 = (b1 << 10) | res[0], r2 = r1 - res[1];
-    for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n_c; i += TT)
-        if ((ckey[i] >> 10) == p2) atomicAdd(&hist[ckey[i] & 1023u], 1u);
-    __syncthreads();
-    find_bin(hist, 1024, r2, sh, res);
-    const uint32_t kthr = (p2 << 10) | res[0], n_tie = res[2], r3 = r2 - res[1];
-    const uint32_t inv_thr = tie_threshold(ckey, cidx, n_c, kthr, n_tie, r3, hist, sh, res);
-    emit_ascending(nullptr, 0, ckey, cidx, n_c, kthr, inv_thr, n_cand, out, hist, sh);
+    select_candidates(ckey, cidx, n_c, k, n_cand, out, hist, sh, res);
 }
 
 }  // namespace

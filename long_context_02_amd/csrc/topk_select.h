@@ -27,22 +27,25 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     return v;
 }
 
-// Exclusive prefix sum of v over the workgroup (thread order); *total gets
-// the sum.  Contains barriers: every thread must call it.
+// Exclusive prefix sum of v over the workgroup of NTH threads (thread
+// order); *total gets the sum.  sh holds NTH/64 + 1 words.  Contains
+// barriers: every thread must call it.
+template <int NTH = TT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+    constexpr int NWV = NTH / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(v);
     if (lane == 63) sh[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        const uint32_t x = lane < NW ? sh[lane] : 0u;
+        const uint32_t x = lane < NWV ? sh[lane] : 0u;
         const uint32_t xi = wave_incl_scan(x);
-        if (lane < NW) sh[lane] = xi - x;
-        if (lane == NW - 1) sh[NW] = xi;
+        if (lane < NWV) sh[lane] = xi - x;
+        if (lane == NWV - 1) sh[NWV] = xi;
     }
     __syncthreads();
     const uint32_t r = sh[wave] + incl - v;
-    *total = sh[NW];
+    *total = sh[NWV];
     __syncthreads();
     return r;
 }
@@ -60,15 +63,16 @@ __device__ __forceinline__ void load4(const float* __restrict__ s, int e, int n,
 
 // Find, over nb histogram bins read in descending bin order, the bin that
 // holds the need-th largest element.  Writes (bin, count above, count in bin)
-// to res.  Every thread must call it; nb <= 4*TT.
+// to res.  Every thread of the NTH-thread workgroup must call it.
+template <int NTH = TT>
 __device__ void find_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh, uint32_t* res) {
-    const int per = (nb + TT - 1) / TT;      // bins per thread (1 or 4)
+    const int per = (nb + NTH - 1) / NTH;    // bins per thread
     const int hi = nb - per * (int)threadIdx.x;  // this thread owns bins [hi-per, hi)
     uint32_t cnt = 0;
     for (int i = 1; i <= per; ++i)
         if (hi - i >= 0) cnt += hist[hi - i];
     uint32_t total;
-    const uint32_t above = block_excl_scan(cnt, sh, &total);
+    const uint32_t above = block_excl_scan<NTH>(cnt, sh, &total);
     if (cnt > 0 && above < need && above + cnt >= need) {
         uint32_t acc = above;
         for (int i = 1; i <= per; ++i) {
@@ -298,7 +302,8 @@ __device__ void select_row(const float* __restrict__ s, int32_t* __restrict__ ou
 // indices: returns inv_thr such that exactly those ties have ~index >= inv_thr
 // (0 when every tie is kept).  Radix select on ~index (larger = lower index)
 // with digits of 12, 10 and 10 bits.  hist needs BINS words.  Every thread of
-// the workgroup must call it.
+// the NTH-thread workgroup must call it.
+template <int NTH = TT>
 __device__ uint32_t tie_threshold(const uint32_t* ckey, const int32_t* cidx, int n_c, uint32_t kthr,
                                   uint32_t n_tie, uint32_t r, uint32_t* hist, uint32_t* sh,
                                   uint32_t* res) {
@@ -308,15 +313,16 @@ __device__ uint32_t tie_threshold(const uint32_t* ckey, const int32_t* cidx, int
     while (shift > 0) {
         const int d = shift == 32 ? 12 : 10;
         const uint32_t nb = 1u << d;
-        for (int i = threadIdx.x; i < (int)nb; i += TT) hist[i] = 0u;
+        for (int i = threadIdx.x; i < (int)nb; i += NTH) hist[i] = 0u;
         __syncthreads();
-        for (int i = threadIdx.x; i < n_c; i += TT) {
+        #pragma unroll 1
+        for (int i = threadIdx.x; i < n_c; i += NTH) {
             const uint32_t inv = ~(uint32_t)cidx[i];
             const bool pre = shift == 32 || (inv >> shift) == prefix;
             if (ckey[i] == kthr && pre) atomicAdd(&hist[(inv >> (shift - d)) & (nb - 1u)], 1u);
         }
         __syncthreads();
-        find_bin(hist, (int)nb, need, sh, res);
+        find_bin<NTH>(hist, (int)nb, need, sh, res);
         need -= res[1];
         prefix = (prefix << d) | res[0];
         shift -= d;
@@ -330,27 +336,31 @@ constexpr int BM_BITS = BINS * 32;  // index window of one bitmap pass
 // (global memory) and the candidates with key > kthr, or key == kthr and
 // ~index >= inv_thr, all below n_cand.  A bitmap over BM_BITS indices at a
 // time (bm: BINS words) and a block scan of the per-thread popcounts give
-// every pick its output slot.  Every thread of the workgroup must call it.
+// every pick its output slot.  Every thread of the NTH-thread workgroup must
+// call it.
+template <int NTH = TT>
 __device__ void emit_ascending(const int32_t* __restrict__ sure, int n_sure, const uint32_t* ckey,
                                const int32_t* cidx, int n_c, uint32_t kthr, uint32_t inv_thr,
                                int n_cand, int32_t* __restrict__ out, uint32_t* bm, uint32_t* sh) {
     const int tid = threadIdx.x;
     uint32_t emitted = 0;
     for (int w0 = 0; w0 < n_cand; w0 += BM_BITS) {
-        for (int i = tid; i < BINS; i += TT) bm[i] = 0u;
+        for (int i = tid; i < BINS; i += NTH) bm[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < n_sure; i += TT) {
+        #pragma unroll 1
+        for (int i = tid; i < n_sure; i += NTH) {
             const int e = sure[i] - w0;
             if (e >= 0 && e < BM_BITS) atomicOr(&bm[e >> 5], 1u << (e & 31));
         }
-        for (int i = tid; i < n_c; i += TT) {
+        #pragma unroll 1
+        for (int i = tid; i < n_c; i += NTH) {
             const uint32_t key = ckey[i];
             const bool take = key > kthr || (key == kthr && ~(uint32_t)cidx[i] >= inv_thr);
             const int e = cidx[i] - w0;
             if (take && e >= 0 && e < BM_BITS) atomicOr(&bm[e >> 5], 1u << (e & 31));
         }
         __syncthreads();
-        constexpr int WPT = BINS / TT;  // bitmap words per thread
+        constexpr int WPT = BINS / NTH;  // bitmap words per thread
         uint32_t m[WPT], cnt = 0;
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
@@ -358,7 +368,7 @@ __device__ void emit_ascending(const int32_t* __restrict__ sure, int n_sure, con
             cnt += __popc(m[j]);
         }
         uint32_t total;
-        uint32_t p = emitted + block_excl_scan(cnt, sh, &total);
+        uint32_t p = emitted + block_excl_scan<NTH>(cnt, sh, &total);
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
             uint32_t x = m[j];
@@ -370,6 +380,72 @@ __device__ void emit_ascending(const int32_t* __restrict__ sure, int n_sure, con
         }
         emitted += total;
     }
+}
+
+// Exact top-k among n_c >= k candidates (keys ckey, token indices cidx, any
+// order) written to out in ascending index order: the k-th key by three radix
+// digits (12, 10, 10 bits), the lowest-index ties, bitmap emission over
+// [0, n_cand).  hist: BINS words of LDS; sh: NTH/64 + 1 words; res: 3.
+template <int NTH = TT>
+__device__ __forceinline__ void select_candidates(const uint32_t* ckey, const int32_t* cidx, int n_c, int k,
+                                  int n_cand, int32_t* __restrict__ out, uint32_t* hist,
+                                  uint32_t* sh, uint32_t* res) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < BINS; i += NTH) hist[i] = 0u;
+    __syncthreads();
+    #pragma unroll 1
+    for (int i = tid; i < n_c; i += NTH) atomicAdd(&hist[ckey[i] >> 20], 1u);
+    __syncthreads();
+    find_bin<NTH>(hist, BINS, (uint32_t)k, sh, res);
+    const uint32_t b1 = res[0], r1 = (uint32_t)k - res[1];
+    for (int i = tid; i < 1024; i += NTH) hist[i] = 0u;
+    __syncthreads();
+    #pragma unroll 1
+    for (int i = tid; i < n_c; i += NTH)
+        if ((ckey[i] >> 20) == b1) atomicAdd(&hist[(ckey[i] >> 10) & 1023u], 1u);
+    __syncthreads();
+    find_bin<NTH>(hist, 1024, r1, sh, res);
+    const uint32_t p2 = (b1 << 10) | res[0], r2 = r1 - res[1];
+    for (int i = tid; i < 1024; i += NTH) hist[i] = 0u;
+    __syncthreads();
+    #pragma unroll 1
+    for (int i = tid; i < n_c; i += NTH)
+        if ((ckey[i] >> 10) == p2) atomicAdd(&hist[ckey[i] & 1023u], 1u);
+    __syncthreads();
+    find_bin<NTH>(hist, 1024, r2, sh, res);
+    const uint32_t kthr = (p2 << 10) | res[0], n_tie = res[2], r3 = r2 - res[1];
+    const uint32_t inv_thr = tie_threshold<NTH>(ckey, cidx, n_c, kthr, n_tie, r3, hist, sh, res);
+    emit_ascending<NTH>(nullptr, 0, ckey, cidx, n_c, kthr, inv_thr, n_cand, out, hist, sh);
+}
+
+// Candidate threshold from a sample of a row's keys: the key of the r-th
+// largest of the S sample keys in skey, rounded down to its top 22 bits, with
+// r = mu + c1 sqrt(mu) + c0 and mu = S k / n_cand (the expected number of
+// samples among the row's top k); 0 (every key passes) when r >= S.  Keys at
+// or above it hold the row's top k unless the sample is far from typical.
+// hist: BINS words; every thread of the NTH-thread workgroup must call it.
+template <int NTH = TT>
+__device__ uint32_t sample_threshold(const uint32_t* skey, int S, int k, int n_cand, float c1,
+                                     float c0, uint32_t* hist, uint32_t* sh, uint32_t* res) {
+    const float mu = (float)S * (float)k / (float)n_cand;
+    const int r = (int)ceilf(mu + c1 * sqrtf(mu) + c0);
+    if (r >= S) return 0u;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < BINS; i += NTH) hist[i] = 0u;
+    __syncthreads();
+    #pragma unroll 1
+    for (int i = tid; i < S; i += NTH) atomicAdd(&hist[skey[i] >> 20], 1u);
+    __syncthreads();
+    find_bin<NTH>(hist, BINS, (uint32_t)r, sh, res);
+    const uint32_t b1 = res[0], r2 = (uint32_t)r - res[1];
+    for (int i = tid; i < 1024; i += NTH) hist[i] = 0u;
+    __syncthreads();
+    #pragma unroll 1
+    for (int i = tid; i < S; i += NTH)
+        if ((skey[i] >> 20) == b1) atomicAdd(&hist[(skey[i] >> 10) & 1023u], 1u);
+    __syncthreads();
+    find_bin<NTH>(hist, 1024, r2, sh, res);
+    return (b1 << 20) | (res[0] << 10);
 }
 
 }  // namespace
