@@ -60,6 +60,7 @@ dsa_status check_attn(const void* q, const void* kv, const int32_t* idx, const v
     if ((long long)B * N * (long long)(d_qk > 0 ? d_qk : 1) >= (1LL << 42)) return DSA_ERR_UNSUPPORTED;
     if (dt == DSA_BF16) {
         if (H != 128 || d_qk != 576 || d_v != 512) return DSA_ERR_UNSUPPORTED;
+        if ((long long)N * 1152 >= (1LL << 31)) return DSA_ERR_UNSUPPORTED;  // 32-bit row offsets
         return DSA_OK;
     }
     if (dt == DSA_F32) {

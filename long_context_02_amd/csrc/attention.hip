@@ -68,6 +68,35 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& x) { return __builtin_b
 // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
 #define DSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at p (raw buffer, 32-bit offsets; a load
+// at an offset at or beyond `bytes` touches no memory and returns zeros).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)p;
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+                 __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes at buffer offset
+// voff + soff land at lds_dst + 16*l.  Issued from inline assembly so that
+// the compiler does not guard later LDS reads of other stages with waits on
+// every load in flight; the ring waits for its own loads (vmcnt) before the
+// barrier that publishes a stage.  No register receives data.
+__device__ __forceinline__ void load_lds16(const i32x4& rsrc, unsigned lds_dst, unsigned voff,
+                                           unsigned soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "m0");
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <bool PARTIAL>
 __global__ __launch_bounds__(NTA) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_attn_bf16(
@@ -166,24 +195,34 @@ void sparse_mla_attn_bf16(
     // direct-to-LDS gather of one tile: wave w brings latent rows 8w..8w+7
     // (one 1 KiB row per instruction, lane l fetching chunk l ^ swz(r)) and
     // the rope parts of rows 8w..8w+7 (lane l: row 8w+l/8, chunk
-    // (l%8) ^ (row%8)); 9 loads per wave and tile.  gather_ids() looks the
-    // rows up (lane l: row 8w + l/8); dma(u) issues load u.
+    // (l%8) ^ (row%8)); 9 loads per wave and tile.  The loads go through a
+    // buffer resource over this sequence's rows (the base stays in SGPRs;
+    // the row offset of a latent load is a scalar).  A tile at or past
+    // n_tiles is still "loaded", with offsets beyond the resource's range:
+    // such loads touch no memory, so every tile issues the same number of
+    // loads and the ring's wait counts do not depend on the position.
+    // gather_id() looks the rows up (lane l: row 8w + l/8); dma(u) issues
+    // load u.
+    const i32x4 kv_rsrc = buffer_rsrc(kv_b, (unsigned)N * (unsigned)(2 * DQK));
+    const int lane16 = lane << 4;
     auto gather_id = [&](int tile) __attribute__((always_inline)) {
         const int r = 8 * wave + (lane >> 3);
         int id = sidx[tile * TK + r];
         if (id < 0 || id >= N) id = dummy;
-        return id;
+        return tile < n_tiles ? id : -1;
     };
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     auto dma = [&](uint8_t* st, int id, int u) __attribute__((always_inline)) {
         if (u < 8) {
-            const int ru = 8 * wave + u;
+            const int ru = 8 * wave_s + u;
             const int idu = __builtin_amdgcn_readlane(id, 8 * u);
-            const uint16_t* src = kv_b + (size_t)idu * DQK + 8 * (lane ^ swz(ru));
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + ru * LAT), 16, 0, 0);
+            const unsigned vo = idu < 0 ? 0x80000000u : (unsigned)(lane16 ^ (swz(ru) << 4));
+            load_lds16(kv_rsrc, lds_addr(st) + ru * LAT, vo, (unsigned)max(idu, 0) * (2 * DQK));
         } else {
             const int r = 8 * wave + (lane >> 3);
-            const uint16_t* src = kv_b + (size_t)id * DQK + 512 + 8 * ((lane & 7) ^ (r & 7));
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + TK * LAT + wave * 1024), 16, 0, 0);
+            const unsigned vo = id < 0 ? 0x80000000u
+                                       : (unsigned)id * (2 * DQK) + 1024 + 16 * ((lane & 7) ^ (r & 7));
+            load_lds16(kv_rsrc, lds_addr(st) + TK * LAT + wave_s * 1024, vo, 0u);
         }
     };
     auto issue = [&](uint8_t* st, int tile) __attribute__((always_inline)) {
@@ -195,7 +234,7 @@ void sparse_mla_attn_bf16(
     // Multiply tile `tile` (in stage st); when nxt is not null, the loads of
     // tile `tile + 3` into nxt are spread over the QK^T steps.
     auto compute = [&](const uint8_t* st, int tile, uint8_t* nxt) __attribute__((always_inline)) {
-        const int nid = nxt ? gather_id(tile + 3) : 0;
+        const int nid = gather_id(tile + 3);
         // validity of this lane's keys 4g..4g+3 and 16+4g..16+4g+3
         const int4 ia = *reinterpret_cast<const int4*>(&sidx[tile * TK + 4 * g]);
         const int4 ib = *reinterpret_cast<const int4*>(&sidx[tile * TK + 16 + 4 * g]);
@@ -213,7 +252,7 @@ void sparse_mla_attn_bf16(
         bf16x8 kf[3][2];
         kf[0][0] = kfrag(0, 0); kf[0][1] = kfrag(1, 0);
         kf[1][0] = kfrag(0, 1); kf[1][1] = kfrag(1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) {
             const int c = ks % 3;
@@ -225,11 +264,10 @@ void sparse_mla_attn_bf16(
             sacc[0][1] = mfma_bf16(kf[c][0], qf[1][ks], sacc[0][1]);
             sacc[1][0] = mfma_bf16(kf[c][1], qf[0][ks], sacc[1][0]);
             sacc[1][1] = mfma_bf16(kf[c][1], qf[1][ks], sacc[1][1]);
-            if (nxt && (ks & 1) == 0 && (ks >> 1) < DMA_PER_TILE) dma(nxt, nid, ks >> 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            if (ks + 2 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if ((ks & 1) == 0 && (ks >> 1) < DMA_PER_TILE) dma(nxt, nid, ks >> 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (nxt) dma(nxt, nid, DMA_PER_TILE - 1);
+        dma(nxt, nid, DMA_PER_TILE - 1);
 
         const int ids[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
         bool ok[8];
@@ -278,32 +316,29 @@ void sparse_mla_attn_bf16(
         bf16x8 vf[3];
         vf[0] = vfrag(0);
         vf[1] = vfrag(1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nv = 0; nv < DV / 16; ++nv) {
             if (nv + 2 < DV / 16) vf[(nv + 2) % 3] = vfrag(nv + 2);
             o[0][nv] = mfma_bf16(pa[0], vf[nv % 3], o[0][nv]);
             o[1][nv] = mfma_bf16(pa[1], vf[nv % 3], o[1][nv]);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-            if (nv + 2 < DV / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // one ring step: wait for tile `it`, publish it with a barrier (which
-    // also tells every wave that the stage read at it-1 is free), then
-    // multiply tile it while refilling that stage with tile it+3
+    // one ring step: wait for tile `it` (the loads of tiles it+1 and it+2 may
+    // stay in flight), publish it with a barrier (which also tells every wave
+    // that the stage read at it-1 is free), then multiply tile it while
+    // refilling that stage with tile it+3
     auto step = [&](uint8_t* cur, uint8_t* nxt, int it) __attribute__((always_inline)) {
         if (it >= n_tiles) return;
-        const int after = min(2, n_tiles - 1 - it);
-        if (after >= 2) DSA_WAIT_VM(2 * DMA_PER_TILE);
-        else if (after == 1) DSA_WAIT_VM(DMA_PER_TILE);
-        else DSA_WAIT_VM(0);
+        DSA_WAIT_VM(2 * DMA_PER_TILE);
         // a barrier that is also a compiler memory barrier (no LDS access moves
         // across it) but, unlike __syncthreads(), waits for no global loads
         // (its own earlier LDS reads are finished first, so no stage a
         // wave is still reading gets refilled)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        compute(cur, it, it + 3 < n_tiles ? nxt : nullptr);
+        compute(cur, it, nxt);
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -315,15 +350,16 @@ void sparse_mla_attn_bf16(
             m_ref[hb] = pass == 0 ? -__builtin_inff() : m_all[hb];
             if (pass == 0) m_all[hb] = -__builtin_inff();
         }
-        if (n_tiles > 0) issue(st0, 0);
-        if (n_tiles > 1) issue(st1, 1);
-        if (n_tiles > 2) issue(st2, 2);
+        issue(st0, 0);
+        issue(st1, 1);
+        issue(st2, 2);
         for (int it = 0; it < n_tiles; it += 4) {
             step(st0, st3, it);
             step(st1, st0, it + 1);
             step(st2, st1, it + 2);
             step(st3, st2, it + 3);
         }
+        DSA_WAIT_VM(0);  // the loads past the last tile land before the stages are reused
         if (pass == 1) break;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {  // per-lane maxima -> max of the head
@@ -513,6 +549,7 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
                             void* workspace, hipStream_t stream) {
     if (k > SLOTS) return DSA_ERR_UNSUPPORTED;
     if (T > 65535 || B > 65535) return DSA_ERR_UNSUPPORTED;
+    if ((size_t)N * (2 * DQK) >= 0x80000000ull) return DSA_ERR_UNSUPPORTED;  // 32-bit gather offsets
     const long long rows = (long long)B * T;
     const int s = attn_num_splits((int)std::min<long long>(rows, 1 << 30), k);
     const float scale_log2 = sm_scale * kLog2e;
