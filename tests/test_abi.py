@@ -103,9 +103,9 @@ def test_topk_rejects_bad_arguments():
 def test_attention_rejects_bad_arguments():
     f = dsa.lib().dsa_sparse_mla_attn
 
-    def call(H=128, dqk=576, dv=512, k=2048, scale=0.04, dt=dsa.BF16, ptrs=None):
+    def call(H=128, dqk=576, dv=512, k=2048, scale=0.04, dt=dsa.BF16, ptrs=None, N=10):
         ptrs = ptrs or [P, P, P, P, None]
-        return f(*ptrs, 1, 1, 10, H, dqk, dv, k, scale, dt, None, 0, None)
+        return f(*ptrs, 1, 1, N, H, dqk, dv, k, scale, dt, None, 0, None)
 
     assert call(ptrs=[P, None, P, P, None]) == 1
     assert call(H=64) == 2 and call(dqk=512) == 2 and call(dv=256) == 2
@@ -113,6 +113,7 @@ def test_attention_rejects_bad_arguments():
     assert call(scale=float("nan")) == 1
     assert call(dt=dsa.FP8_E4M3FN) == 2
     assert call(H=16, dqk=80, dv=96, dt=dsa.F32) == 2     # d_v > d_qk
+    assert call(N=(1 << 31) // 1152 + 1) == 2             # bf16 rows beyond 32-bit offsets
 
 
 def test_indexer_select_rejects_bad_arguments():
