@@ -134,16 +134,9 @@ void sparse_mla_attn_bf16(
     }
     if (my_last >= 0) atomicMax(&s_last, my_last);
 
-    // ---- this wave's 32 query heads (two blocks of 16) as B operands
-    // (k = 8*(l/16)+j within each 32-wide step of d)
+    // this wave's 32 query heads (two blocks of 16) as B operands; loaded
+    // once the first gather loads are in flight
     bf16x8 qf[2][DQK / 32];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const uint16_t* qh = q + (row * H + 32 * wave + 16 * hb + m) * DQK + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < DQK / 32; ++ks)
-            qf[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
-    }
     __syncthreads();
     const int last = s_last;
     const int n_tiles = (last + TK) / TK;  // 0 when no slot is valid
@@ -272,17 +265,17 @@ void sparse_mla_attn_bf16(
         const int ids[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
         bool ok[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ok[i] = ids[i] >= 0 && ids[i] < N;
+        for (int i = 0; i < 8; ++i) ok[i] = (unsigned)ids[i] < (unsigned)N;
         bf16x8 pa[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
+            // x = s * scale in base 2 (-inf for invalid slots); products are
+            // never signalling NaNs, so the maxima need no canonicalisation
             float x[8];
-            float mx = -__builtin_inff();
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                x[i] = ok[i] ? sacc[i >> 2][hb][i & 3] * scale_log2 : -__builtin_inff();
-                mx = fmaxf(mx, x[i]);
-            }
+            for (int i = 0; i < 8; ++i) x[i] = ok[i] ? sacc[i >> 2][hb][i & 3] * scale_log2 : -__builtin_inff();
+            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             // per-lane bookkeeping; the max over the head's four lane groups is
             // only needed to fix the reference on the first tile with a valid key
             if (m_ref[hb] == -__builtin_inff()) {
@@ -292,10 +285,16 @@ void sparse_mla_attn_bf16(
             }
             m_all[hb] = fmaxf(m_all[hb], mx);
             over |= mx > m_ref[hb] + REF_GAP;
+            // exp2(-inf - m) = 0 for invalid slots; a head with no valid key so
+            // far (m_ref = -inf) subtracts 0 instead, so its weights stay 0.
+            // v_exp_f32 without range reduction: the argument is at most
+            // REF_GAP (larger ones make the pass rerun) and results below the
+            // normal range flush to 0, which the weights can afford.
+            const float mr = m_ref[hb] == -__builtin_inff() ? 0.f : m_ref[hb];
             float p[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                p[i] = ok[i] ? exp2f(x[i] - m_ref[hb]) : 0.f;
+                p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
                 l_part[hb] += p[i];
             }
             pa[hb] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
@@ -341,6 +340,23 @@ void sparse_mla_attn_bf16(
         compute(cur, it, nxt);
     };
 
+    // the first pass's ring prologue, then Q (k = 8*(l/16)+j within each
+    // 32-wide step of d) while those loads are in flight
+    issue(st0, 0);
+    issue(st1, 1);
+    issue(st2, 2);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const uint16_t* qh = q + (row * H + 32 * wave + 16 * hb + m) * DQK + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < DQK / 32; ++ks)
+            qf[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
+    }
+    // all of Q is in registers before the loop: the waits the compiler would
+    // otherwise place at Q's first uses inside the loop would also wait for
+    // the gather loads it does not know about
+    DSA_WAIT_VM(0);
+
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -350,9 +366,11 @@ void sparse_mla_attn_bf16(
             m_ref[hb] = pass == 0 ? -__builtin_inff() : m_all[hb];
             if (pass == 0) m_all[hb] = -__builtin_inff();
         }
-        issue(st0, 0);
-        issue(st1, 1);
-        issue(st2, 2);
+        if (pass == 1) {
+            issue(st0, 0);
+            issue(st1, 1);
+            issue(st2, 2);
+        }
         for (int it = 0; it < n_tiles; it += 4) {
             step(st0, st3, it);
             step(st1, st0, it + 1);
