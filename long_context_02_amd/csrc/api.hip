@@ -57,6 +57,7 @@ dsa_status check_attn(const void* q, const void* kv, const int32_t* idx, const v
     if (!std::isfinite(sm_scale)) return DSA_ERR_INVALID_ARG;
     if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
     if (B > 65535 || T > 65535) return DSA_ERR_UNSUPPORTED;
+    if ((long long)B * T > 0x7fffffffLL) return DSA_ERR_UNSUPPORTED;  // one workgroup id per row
     if ((long long)B * N * (long long)(d_qk > 0 ? d_qk : 1) >= (1LL << 42)) return DSA_ERR_UNSUPPORTED;
     if (dt == DSA_BF16) {
         if (H != 128 || d_qk != 576 || d_v != 512) return DSA_ERR_UNSUPPORTED;

@@ -97,12 +97,24 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (XCD = linear
+// id % 8), each with its own L2.  Map linear ids so that every XCD works
+// through a contiguous range of (query row, slot range) items: the slot
+// ranges of one query row, which all read that row's Q, then run on one XCD.
+// Ids past the last multiple of 8 keep their own number.
+__device__ __forceinline__ unsigned xcd_contiguous(unsigned id, unsigned total) {
+    const unsigned full = total & ~7u;
+    if (id >= full) return id;
+    return (id & 7u) * (full >> 3) + (id >> 3);
+}
+
 template <bool PARTIAL>
 __global__ __launch_bounds__(NTA) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_ml, int T, int N, int k, int slots_per_split, float scale_log2) {
+    float* __restrict__ part_ml, int T, int N, int k, int nsplit, int slots_per_split,
+    float scale_log2) {
     // four ring stages, separate objects so that the compiler can tell the
     // stage being read from the stages being filled
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
@@ -113,9 +125,12 @@ void sparse_mla_attn_bf16(
     __shared__ int s_last;
     __shared__ int s_redo;
 
-    const int split = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
-    const int nsplit = gridDim.x;
-    const size_t row = (size_t)b * T + t;
+    // (split batches only: causal prefill rows differ in length, and giving
+    // each XCD a contiguous range of them would unbalance the XCDs)
+    const unsigned item = PARTIAL ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int split = (int)(item % (unsigned)nsplit);
+    const size_t row = item / (unsigned)nsplit;
+    const int b = (int)(row / (unsigned)T);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, g = lane >> 4;
     const int slot0 = split * slots_per_split;
@@ -575,8 +590,8 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
     const auto* kk = static_cast<const uint16_t*>(kv);
     auto* oo = static_cast<uint16_t*>(out);
     if (s <= 1) {
-        sparse_mla_attn_bf16<false><<<dim3(1, T, B), NTA, 0, stream>>>(
-            qq, kk, idx, oo, lse, nullptr, nullptr, T, N, k, k, scale_log2);
+        sparse_mla_attn_bf16<false><<<dim3((unsigned)rows), NTA, 0, stream>>>(
+            qq, kk, idx, oo, lse, nullptr, nullptr, T, N, k, 1, k, scale_log2);
         return launch_status();
     }
     const int per = ((k + s - 1) / s + TK - 1) / TK * TK;
@@ -584,8 +599,8 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
     uint16_t* part_o = static_cast<uint16_t*>(workspace);
     float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                               align_up((size_t)rows * s * H * DV * sizeof(uint16_t)));
-    sparse_mla_attn_bf16<true><<<dim3(s_eff, T, B), NTA, 0, stream>>>(
-        qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, per, scale_log2);
+    sparse_mla_attn_bf16<true><<<dim3((unsigned)(rows * s_eff)), NTA, 0, stream>>>(
+        qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, s_eff, per, scale_log2);
     dsa_status st = launch_status();
     if (st != DSA_OK) return st;
     attn_combine<<<dim3((unsigned)rows, H / 4), 512, 0, stream>>>(part_o, part_ml, oo, lse, s_eff);
