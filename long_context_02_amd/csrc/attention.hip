@@ -462,27 +462,53 @@ void sparse_mla_attn_bf16(
 __global__ __launch_bounds__(512) void attn_combine(const uint16_t* __restrict__ part_o,
                                                    const float* __restrict__ part_ml,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                   int nsplit) {
-    const size_t row = blockIdx.x;
-    const int h = blockIdx.y * 4 + (threadIdx.x >> 7);
+                                                   int nsplit, int rows) {
+    // 32 workgroups (4 heads each) per row.  When the row count is a multiple
+    // of 8, the attention kernel ran rows [x*rows/8, (x+1)*rows/8) on XCD x;
+    // merge them there too, where their partials were just written.
+    unsigned r, hg;
+    if ((rows & 7) == 0) {
+        const unsigned x = blockIdx.x & 7u, j = blockIdx.x >> 3;
+        r = x * (unsigned)(rows >> 3) + (j >> 5);
+        hg = j & 31u;
+    } else {
+        r = blockIdx.x >> 5;
+        hg = blockIdx.x & 31u;
+    }
+    const size_t row = r;
+    const int h = hg * 4 + (threadIdx.x >> 7);
     const int v = (threadIdx.x & 127) * 4;
+    // every load first (at most 8 slot ranges: k <= 2048, >= 256 slots each),
+    // then the arithmetic
+    constexpr int MAXS = 8;
+    float mv[MAXS], lv[MAXS];
+    uint2 xv[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+        if (s < nsplit) {
+            const size_t pb = (row * nsplit + s) * H + h;
+            mv[s] = part_ml[pb * 2];
+            lv[s] = part_ml[pb * 2 + 1];
+            xv[s] = *reinterpret_cast<const uint2*>(part_o + pb * DV + v);
+        } else {
+            mv[s] = -__builtin_inff();
+            lv[s] = 0.f;
+            xv[s] = uint2{0u, 0u};
+        }
+    }
     float M = -__builtin_inff();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((row * nsplit + s) * H + h) * 2]);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) M = fmaxf(M, mv[s]);
     float L = 0.f;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < nsplit; ++s) {
-            const size_t pb = (row * nsplit + s) * H + h;
-            const float ms = part_ml[pb * 2];
-            if (ms == -__builtin_inff()) continue;
-            const float f = part_ml[pb * 2 + 1] * exp2f(ms - M);
-            L += f;
-            const uint2 x = *reinterpret_cast<const uint2*>(part_o + pb * DV + v);
-            acc.x += __uint_as_float(x.x << 16) * f;
-            acc.y += __uint_as_float(x.x & 0xffff0000u) * f;
-            acc.z += __uint_as_float(x.y << 16) * f;
-            acc.w += __uint_as_float(x.y & 0xffff0000u) * f;
-        }
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+        const float f = mv[s] == -__builtin_inff() ? 0.f : lv[s] * exp2f(mv[s] - M);
+        L += f;
+        acc.x += __uint_as_float(xv[s].x << 16) * f;
+        acc.y += __uint_as_float(xv[s].x & 0xffff0000u) * f;
+        acc.z += __uint_as_float(xv[s].y << 16) * f;
+        acc.w += __uint_as_float(xv[s].y & 0xffff0000u) * f;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint2 pk;
@@ -603,7 +629,8 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
         qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, s_eff, per, scale_log2);
     dsa_status st = launch_status();
     if (st != DSA_OK) return st;
-    attn_combine<<<dim3((unsigned)rows, H / 4), 512, 0, stream>>>(part_o, part_ml, oo, lse, s_eff);
+    attn_combine<<<dim3((unsigned)rows * (H / 4)), 512, 0, stream>>>(part_o, part_ml, oo, lse, s_eff,
+                                                                    (int)rows);
     return launch_status();
 }
 
