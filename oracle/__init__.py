@@ -8,6 +8,10 @@ library (``long_context_02_amd``) and imports nothing from it.
 
 Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   fp8.e4m3_decode / e4m3_encode   pinned (torch's e4m3fn cast, exhaustive)
+  fp8.quantize_rows               pinned (amax element -> +-448, power-of-two
+                                  scale invariance, zero rows, half-step error)
+  cache_append                    pinned (untouched rows, per-sequence
+                                  positions, skipped out-of-range rows)
   index_scores                    pinned (hand 4-token example, integer dot
                                   identity, pure-Python brute force)
   topk_select                     pinned (full sort by (score desc, index asc),
@@ -18,7 +22,7 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   dsa_forward                     pinned (composition; chunked prefill equals
                                   the tail rows of a full prefill)
 """
-from .fp8 import e4m3_decode, e4m3_encode, dequantize, E4M3_MAX  # noqa: F401
+from .fp8 import e4m3_decode, e4m3_encode, dequantize, quantize_rows, E4M3_MAX  # noqa: F401
 from .dsa import (  # noqa: F401
     index_scores,
     index_scores_row,
@@ -28,4 +32,5 @@ from .dsa import (  # noqa: F401
     sparse_mqa_attention_row,
     dsa_forward,
     default_sm_scale,
+    cache_append,
 )

@@ -23,7 +23,7 @@ definitions on the pages:
   one latent vector per selected token is shared by every query head; the key
   is the whole latent+rope vector, the value is its leading d_v latent part.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
 inclusive causal boundary s <= q_offset + t; fewer than k candidates select
 all of them and pad with -1; ties go to the lower index; indices come out
 ascending; NaN ranks below every number; -0 equals +0.
@@ -243,3 +243,38 @@ def dsa_forward(q_idx, k_idx, w, q, kv, *, k, q_offset, d_v, sm_scale,
 def default_sm_scale(d_qk: int) -> float:
     """Softmax scale 1/sqrt(d_qk) (the rule the small fp32 workload states)."""
     return 1.0 / math.sqrt(d_qk)
+
+
+# --------------------------------------------------------------------------
+# Cache append (the step before the path at decode)
+# --------------------------------------------------------------------------
+def cache_append(k_new, kv_new, k_cache, k_cache_scale, kv_cache, pos):
+    """Append new tokens to a sequence batch's caches; returns updated copies.
+
+    The indexer keys are kept per token in FP8 and the latent entries c_s in
+    the attention dtype ("Paper Breakdown: DeepSeek-V3.2", section 2
+    "Architecture: DSA (§2.1)": FP8 indexer, and the latent entry c_s each
+    selected token contributes).  New token t of sequence b goes to row
+    pos[b] + t: its indexer key row k_new[b,t] (float32) is quantised with
+    quantize_rows into k_cache / k_cache_scale, and its latent row
+    kv_new[b,t] is copied into kv_cache unchanged.  Rows whose position falls
+    outside [0, N) are dropped; every other cache row keeps its contents.
+    """
+    from .fp8 import quantize_rows
+
+    k_new = np.asarray(k_new, dtype=np.float32)
+    kc = np.array(k_cache, copy=True)
+    ks = np.array(k_cache_scale, copy=True)
+    kvc = np.array(kv_cache, copy=True)
+    B, T, _ = k_new.shape
+    N = kc.shape[1]
+    for b in range(B):
+        for t in range(T):
+            p = int(pos[b]) + t
+            if p < 0 or p >= N:
+                continue
+            codes, scale = quantize_rows(k_new[b, t])
+            kc[b, p] = codes
+            ks[b, p] = scale
+            kvc[b, p] = kv_new[b, t]
+    return kc, ks, kvc

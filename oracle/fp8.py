@@ -70,3 +70,24 @@ def dequantize(codes, scale) -> np.ndarray:
     ``scale`` broadcasts over the trailing (feature) dimension.
     """
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def quantize_rows(x):
+    """Per-row FP8 quantisation of float32 rows ``x[..., d]``.
+
+    One float32 scale per row maps the row's largest magnitude onto the
+    largest e4m3fn value: scale = amax / 448 (float32 division, correctly
+    rounded), or 1 for a row of zeros; each element becomes
+    encode(x / scale), the quotient again a correctly rounded float32.  The
+    pages fix only that the indexer runs in FP8 ("Paper Breakdown:
+    DeepSeek-V3.2", section 2 "Architecture: DSA (§2.1)", the note under the
+    index-score formula); the per-token amax/448 scale is the reading used
+    for every FP8 operand here.  Rows must be finite.
+
+    Returns (codes uint8 [..., d], scale float32 [...]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
+    return e4m3_encode(y.astype(np.float64)), scale

@@ -7,6 +7,7 @@ import pytest
 import oracle.dsa as od
 import oracle.fp8 as of
 import test_oracle_attn as ta
+import test_oracle_cache as tc
 import test_oracle_forward as tf
 import test_oracle_fp8 as t8
 import test_oracle_indexer as ti
@@ -112,3 +113,37 @@ def test_topk_mutants_caught(monkeypatch, golden_dir, mutant):
 def test_attention_mutants_caught(monkeypatch, golden_dir, mutant):
     monkeypatch.setattr(od, "sparse_mqa_attention_row", mutant)
     assert _fails(ATTN_PINS, golden_dir)
+
+
+_ORIG_QUANT = of.quantize_rows
+
+
+def _scale_447(x):
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(447.0), np.float32(1.0)).astype(np.float32)
+    return of.e4m3_encode((x / scale[..., None]).astype(np.float64)), scale
+
+
+def _truncating(x):
+    codes, scale = _ORIG_QUANT(x)
+    y = (np.asarray(x, np.float32) / scale[..., None]).astype(np.float64)
+    dec = of.e4m3_decode(codes)
+    # step toward zero wherever round-to-nearest went away from zero
+    away = np.abs(dec) > np.abs(y)
+    return np.where(away & ((codes & 0x7F) > 0), codes - 1, codes).astype(np.uint8), scale
+
+
+@pytest.mark.parametrize("mutant", [_scale_447, _truncating])
+def test_quantize_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(tc, "quantize_rows", mutant)
+    pins = [tc.test_largest_element_maps_to_448, tc.test_power_of_two_scale_invariance,
+            tc.test_zero_rows, tc.test_half_step_error_bound, tc.test_matches_torch_composition]
+    assert _fails(pins, golden_dir)
+
+
+def test_append_position_mutant_caught(monkeypatch, golden_dir):
+    orig = od.cache_append
+    monkeypatch.setattr(tc.oracle, "cache_append",
+                        lambda k, kv, kc, ks, kvc, pos: orig(k, kv, kc, ks, kvc, np.asarray(pos) + 1))
+    assert _fails([tc.test_cache_append_bookkeeping], golden_dir)
