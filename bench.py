@@ -25,6 +25,7 @@ summary was taken on the current kernel source, else it is null.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -45,7 +46,8 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-KERNEL_SOURCES = {"select": ("indexer.hip", "topk.hip", "indexer_math.h", "topk_select.h"),
+KERNEL_SOURCES = {"cache_append": ("cache.hip",),
+                  "select": ("indexer.hip", "topk.hip", "indexer_math.h", "topk_select.h"),
                   "indexer": ("indexer.hip", "indexer_math.h", "topk_select.h"),
                   "topk": ("topk.hip", "indexer_math.h", "topk_select.h"),
                   "attention": ("attention.hip",)}
@@ -194,6 +196,45 @@ def timed_sequence(parts, steps, warmup, stream):
     torch.cuda.synchronize()
     return {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
             for j, name in enumerate(names)}
+
+
+def time_cache_append(wl, g, steps, stream):
+    """dsa_cache_append of B*T new tokens at rows q_offset.. of each sequence
+    (after the timed steps; it overwrites those cache rows).  HBM-bound:
+    bytes = new key rows read + key codes/scales written + latent rows read
+    and written + positions."""
+    dev = g["kv"].device
+    gen = torch.Generator(device=dev).manual_seed(1)
+    k_new = torch.randn(wl.B, wl.T, wl.d_I, generator=gen, device=dev)
+    kv_new = torch.randn(wl.B, wl.T, wl.d_qk, generator=gen, device=dev).to(g["kv"].dtype)
+    pos = torch.full((wl.B,), wl.q_offset, dtype=torch.int32, device=dev)
+
+    dsa.cache_append(k_new, kv_new, g["k_idx"], g["k_idx_scale"], g["kv"], pos)  # checks the arguments
+    # then the entry point itself with prepared arguments, so that the host
+    # keeps ahead of this short kernel
+    L = dsa.lib()
+    ks = g["k_idx_scale"]
+    fp8 = ks is not None
+    args = [ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(kv_new.data_ptr()),
+            ctypes.c_void_p(g["k_idx"].data_ptr()), ctypes.c_void_p(ks.data_ptr()) if fp8 else None,
+            ctypes.c_void_p(g["kv"].data_ptr()), ctypes.c_void_p(pos.data_ptr()),
+            wl.B, wl.T, wl.N, wl.d_I, wl.d_qk, dsa.FP8_E4M3FN if fp8 else dsa.F32,
+            dsa.BF16 if g["kv"].dtype == torch.bfloat16 else dsa.F32,
+            ctypes.c_void_p(stream.cuda_stream)]
+
+    def fn():
+        L.dsa_cache_append(*args)
+
+    for _ in range(3):
+        fn()
+    ms = timed(fn, 10 * steps, stream)
+    rows = wl.B * wl.T
+    kv_row = wl.d_qk * g["kv"].element_size()
+    nbytes = rows * (4 * wl.d_I + ((wl.d_I + 4) if fp8 else 4 * wl.d_I) + 2 * kv_row) + 4 * wl.B
+    ach = nbytes / (ms / 1e3) / 1e9
+    return {"ms": round(ms, 4), "tokens": rows, "bound": "hbm", "achieved": round(ach, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+            "algorithmic": nbytes}
 
 
 def cpu_baseline(wl, g, budget_s):
@@ -346,6 +387,9 @@ def main():
         "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 4),
                           "frac": round(t_roof / (ms / 1e3), 4)},
     }
+    # the step before the path (not part of the step): appending this step's
+    # new tokens (one per query token) to the key and latent caches
+    line["next"] = {"cache_append": time_cache_append(wl, g, args.steps, stream)}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl, g, args.cpu_budget)

@@ -193,6 +193,34 @@ DSA_API dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Cache append, the step before the path at decode.  Each token keeps its
+ * indexer key, in FP8 ("Paper Breakdown: DeepSeek-V3.2", section 2
+ * "Architecture: DSA (§2.1)": the indexer runs in FP8), and its latent entry
+ * c_s (same section, the attention formula).  New token t of sequence b is
+ * written to cache row pos[b] + t:
+ *  k_new         [B,T,d_I]  f32        indexer keys of the new tokens
+ *  kv_new        [B,T,d_qk] bf16/f32   latent rows of the new tokens (attn_dtype)
+ *  k_cache       [B,N,d_I]  FP8 codes or f32 (idx_dtype), updated in place
+ *  k_cache_scale [B,N]      f32        per-token scale (FP8 only; NULL for f32)
+ *  kv_cache      [B,N,d_qk] attn_dtype, updated in place
+ *  pos           [B]        int32      row of each sequence's first new token
+ * FP8: scale = amax / 448 (IEEE float32 division; 1 for a row of zeros) and
+ * code = round-to-nearest-even e4m3fn of clamp(x / scale, -448, 448), the
+ * quotient again an IEEE float32 division; this is the per-token scaling the
+ * FP8 indexer operands use.  f32 keys and all latent rows are copied
+ * unchanged.  Rows whose position lies outside [0, N) are dropped (pos is
+ * device data and is not otherwise checked); no other cache row is touched.
+ * Key rows must be finite.  Supported: (idx_dtype, d_I) = (FP8_E4M3FN, 128)
+ * or (F32, 1..256); (attn_dtype, d_qk) = (BF16, 576) or (F32, 1..256).
+ * Positions of one call must not repeat within a sequence's cache rows
+ * (distinct t give distinct rows).
+ */
+DSA_API dsa_status dsa_cache_append(const float* k_new, const void* kv_new, void* k_cache,
+                                    float* k_cache_scale, void* kv_cache, const int32_t* pos,
+                                    int B, int T, int N, int d_I, int d_qk,
+                                    dsa_dtype idx_dtype, dsa_dtype attn_dtype, void* stream);
+
+/*
  * Workspace bytes needed by op (a dsa_op) for these sizes; 0 means none.
  * Returns (size_t)-1 for arguments that no call would accept.
  */

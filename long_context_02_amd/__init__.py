@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "DSAError", "lib", "lib_path", "indexer_scores", "topk_select", "sparse_mla_attn",
-    "forward", "indexer_select", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD", "OP_SELECT",
+    "forward", "indexer_select", "cache_append", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD",
+    "OP_SELECT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_forward.restype = ci
     L.dsa_indexer_select.argtypes = [vp, fp, vp, fp, fp, i32p, ci, ci, ci, ci, ci, ci, ci, ci, vp, sz, vp]
     L.dsa_indexer_select.restype = ci
+    L.dsa_cache_append.argtypes = [fp, vp, vp, fp, vp, i32p, ci, ci, ci, ci, ci, ci, ci, vp]
+    L.dsa_cache_append.restype = ci
     L.dsa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     L.dsa_workspace_size.restype = sz
     L.dsa_status_string.argtypes = [ci]
@@ -289,3 +292,40 @@ def forward(q_idx, k_idx, w, q, kv, *, k: int, q_offset: int, d_v: int, sm_scale
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _raise("dsa_forward", st)
     return out, lse_t, idx_t
+
+
+def cache_append(k_new: torch.Tensor, kv_new: torch.Tensor, k_cache: torch.Tensor,
+                 k_cache_scale: Optional[torch.Tensor], kv_cache: torch.Tensor,
+                 pos: torch.Tensor) -> None:
+    """Write new tokens into the caches in place: token t of sequence b goes
+    to row pos[b] + t (rows outside [0, N) are dropped).  FP8 key caches
+    (uint8 codes with float32 per-token scales) get the keys quantised with
+    scale = amax / 448; float32 key caches and the latent cache get copies.
+
+    k_new [B,T,d_I] float32, kv_new [B,T,d_qk] (kv_cache's dtype),
+    k_cache [B,N,d_I] uint8/float8_e4m3fn or float32, k_cache_scale [B,N]
+    float32 (FP8 only, else None), kv_cache [B,N,d_qk] bfloat16/float32,
+    pos [B] int32 (device)."""
+    dev = k_new.device
+    _check("k_new", k_new, torch.float32, None, dev)
+    B, T, d_I = k_new.shape
+    idt = _idx_dtype(k_cache)
+    _check("k_cache", k_cache, None, None, dev)
+    N = k_cache.shape[1]
+    if k_cache.dim() != 3 or k_cache.shape[0] != B or k_cache.shape[2] != d_I:
+        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected ({B}, N, {d_I})")
+    if idt == FP8_E4M3FN:
+        _check("k_cache_scale", k_cache_scale, torch.float32, (B, N), dev)
+    elif k_cache_scale is not None:
+        raise ValueError("k_cache_scale must be None for a float32 key cache")
+    adt = _attn_dtype(kv_cache)
+    _check("kv_cache", kv_cache, None, None, dev)
+    if kv_cache.dim() != 3 or kv_cache.shape[:2] != (B, N):
+        raise ValueError(f"kv_cache has shape {tuple(kv_cache.shape)}, expected ({B}, {N}, d_qk)")
+    d_qk = kv_cache.shape[2]
+    _check("kv_new", kv_new, kv_cache.dtype, (B, T, d_qk), dev)
+    _check("pos", pos, torch.int32, (B,), dev)
+    with torch.cuda.device(dev):
+        st = lib().dsa_cache_append(_ptr(k_new), _ptr(kv_new), _ptr(_codes(k_cache)), _ptr(k_cache_scale),
+                                    _ptr(kv_cache), _ptr(pos), B, T, N, d_I, d_qk, idt, adt, _stream(dev))
+    _raise("dsa_cache_append", st)

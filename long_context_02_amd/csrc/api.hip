@@ -131,7 +131,7 @@ dsa_status run_attn(const void* q, const void* kv, const int32_t* idx, void* out
 
 extern "C" {
 
-int dsa_version(void) { return (1 << 16) | 0; }
+int dsa_version(void) { return (1 << 16) | 1; }
 
 const char* dsa_status_string(dsa_status s) {
     switch (s) {
@@ -241,6 +241,43 @@ dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* 
                     idx_dtype, workspace, s);
     if (st != DSA_OK) return st;
     return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, attn_w, s);
+}
+
+dsa_status dsa_cache_append(const float* k_new, const void* kv_new, void* k_cache,
+                            float* k_cache_scale, void* kv_cache, const int32_t* pos, int B, int T,
+                            int N, int d_I, int d_qk, dsa_dtype idx_dtype, dsa_dtype attn_dtype,
+                            void* stream) {
+    if (!k_new || !kv_new || !k_cache || !kv_cache || !pos) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(kv_new) || !aligned16(k_cache) || !aligned16(kv_cache) ||
+        !aligned16(pos) || (k_cache_scale && !aligned16(k_cache_scale)))
+        return DSA_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || N < 1) return DSA_ERR_INVALID_ARG;
+    if ((long long)B * N * 1152 >= (1LL << 46) || (long long)B * T >= (1LL << 31))
+        return DSA_ERR_UNSUPPORTED;
+    bool fp8;
+    if (idx_dtype == DSA_FP8_E4M3FN) {
+        if (!k_cache_scale) return DSA_ERR_INVALID_ARG;
+        if (d_I != 128) return DSA_ERR_UNSUPPORTED;
+        fp8 = true;
+    } else if (idx_dtype == DSA_F32) {
+        if (k_cache_scale) return DSA_ERR_INVALID_ARG;
+        if (d_I < 1 || d_I > 256) return DSA_ERR_UNSUPPORTED;
+        fp8 = false;
+    } else {
+        return idx_dtype == DSA_BF16 ? DSA_ERR_UNSUPPORTED : DSA_ERR_INVALID_ARG;
+    }
+    int row_bytes;
+    if (attn_dtype == DSA_BF16) {
+        if (d_qk != 576) return DSA_ERR_UNSUPPORTED;
+        row_bytes = 576 * 2;
+    } else if (attn_dtype == DSA_F32) {
+        if (d_qk < 1 || d_qk > 256) return DSA_ERR_UNSUPPORTED;
+        row_bytes = d_qk * 4;
+    } else {
+        return attn_dtype == DSA_FP8_E4M3FN ? DSA_ERR_UNSUPPORTED : DSA_ERR_INVALID_ARG;
+    }
+    return launch_cache_append(k_new, kv_new, k_cache, k_cache_scale, kv_cache, pos, B, T, N, d_I,
+                               row_bytes, fp8, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -92,6 +92,13 @@ dsa_status launch_attn_f32(const float* q, const float* kv, const int32_t* idx, 
                            float* lse, int B, int T, int N, int H, int d_qk, int d_v, int k,
                            float sm_scale, hipStream_t stream);
 
+// ---- cache append (cache.hip) ---------------------------------------------
+// fp8: quantise the key rows (d_i = 128) into codes + scales; otherwise copy
+// f32 key rows.  Latent rows are copied as kv_row_bytes bytes.
+dsa_status launch_cache_append(const float* k_new, const void* kv_new, void* k_cache, float* k_scale,
+                               void* kv_cache, const int32_t* pos, int B, int T, int N, int d_i,
+                               int kv_row_bytes, bool fp8, hipStream_t stream);
+
 inline dsa_status launch_status() {
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

@@ -136,3 +136,20 @@ def test_forward_rejects_small_workspace():
     st = f(P, P, P, P, P, P, P, P, None, None, 1, 4, 8, 8, 128, 128, 576, 512, 4, 4, 0.04,
            dsa.FP8_E4M3FN, dsa.BF16, P, 16, None)
     assert st == 3
+
+
+def test_cache_append_rejects_bad_arguments():
+    f = dsa.lib().dsa_cache_append
+
+    def call(ptrs=None, d_I=128, d_qk=576, idt=dsa.FP8_E4M3FN, adt=dsa.BF16, B=2, T=1, N=8):
+        ptrs = ptrs or [P, P, P, P, P, P]
+        return f(*ptrs, B, T, N, d_I, d_qk, idt, adt, None)
+
+    assert call(ptrs=[None, P, P, P, P, P]) == 1
+    assert call(ptrs=[P, P, P, P, P, None]) == 1          # no positions
+    assert call(ptrs=[P, P, P, None, P, P]) == 1          # FP8 needs the scales
+    assert call(idt=dsa.F32, d_I=32) == 1                 # f32 keys take no scales
+    assert call(d_I=64) == 2 and call(d_qk=512) == 2
+    assert call(adt=dsa.F32, d_qk=300) == 2
+    assert call(idt=dsa.BF16) == 2 and call(adt=dsa.FP8_E4M3FN) == 2
+    assert call(B=0) == 1 and call(T=0) == 1
