@@ -12,6 +12,10 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
                                   scale invariance, zero rows, half-step error)
   cache_append                    pinned (untouched rows, per-sequence
                                   positions, skipped out-of-range rows)
+  indexer_kl (dense, sparse)      pinned (torch kl_div + float64 autograd,
+                                  p = softmax(I) gives 0, one-hot closed form,
+                                  finite differences, shift invariance,
+                                  sparse over all candidates equals dense)
   index_scores                    pinned (hand 4-token example, integer dot
                                   identity, pure-Python brute force)
   topk_select                     pinned (full sort by (score desc, index asc),
@@ -33,4 +37,7 @@ from .dsa import (  # noqa: F401
     dsa_forward,
     default_sm_scale,
     cache_append,
+    indexer_kl,
+    indexer_kl_dense_row,
+    indexer_kl_sparse_row,
 )

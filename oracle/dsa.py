@@ -278,3 +278,77 @@ def cache_append(k_new, kv_new, k_cache, k_cache_scale, kv_cache, pos):
             ks[b, p] = scale
             kvc[b, p] = kv_new[b, t]
     return kc, ks, kvc
+
+
+# --------------------------------------------------------------------------
+# Indexer alignment loss (continued pre-training)
+# --------------------------------------------------------------------------
+# "Paper Breakdown: DeepSeek-V3.2", section 2, "Continued Pre-Training
+# (§2.1.1)": the dense warm-up trains the indexer with
+#     L^I = sum_t KL(p_{t,:} || Softmax(I_{t,:})),
+# and sparse training keeps the KL objective on the selected set S_t only.
+# Readings: the softmax runs over the row's causal candidates (dense) or over
+# S_t (sparse); the target p is taken as given (no renormalisation), so the
+# loss of a row is sum_s p_s (log p_s - log q_s) over the entries with
+# p_s > 0 (0 log 0 = 0) and its gradient with respect to I_s is
+# P q_s - p_s with P = sum_s p_s (q_s - p_s for a distribution).
+
+def _kl_terms(I, p):
+    I = np.asarray(I, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    if I.size == 0:
+        return 0.0, np.zeros(0)
+    m = np.max(I)
+    lse = m + math.log(np.sum(np.exp(I - m)))
+    logq = I - lse
+    q = np.exp(logq)
+    pos = p > 0
+    loss = float(np.sum(p[pos] * (np.log(p[pos]) - logq[pos])))
+    grad = np.sum(p) * q - p
+    return loss, grad
+
+
+def indexer_kl_dense_row(I_row, p_row, n_cand):
+    """Loss and gradient (w.r.t. the row's scores) of KL(p || softmax(I))
+    over the causal candidates s < n_cand; the gradient is 0 elsewhere."""
+    loss, g = _kl_terms(np.asarray(I_row)[:n_cand], np.asarray(p_row)[:n_cand])
+    grad = np.zeros(len(I_row))
+    grad[:n_cand] = g
+    return loss, grad
+
+
+def indexer_kl_sparse_row(I_row, idx_row, p_sel):
+    """Loss and per-slot gradient of the KL restricted to the selected set:
+    slot i holds token idx_row[i] with target p_sel[i]; slots whose index is
+    outside [0, N) are skipped (gradient 0); duplicates count once per slot."""
+    I_row = np.asarray(I_row, dtype=np.float64)
+    idx_row = np.asarray(idx_row)
+    ok = (idx_row >= 0) & (idx_row < I_row.size)
+    loss, g = _kl_terms(I_row[idx_row[ok]], np.asarray(p_sel, dtype=np.float64)[ok])
+    grad = np.zeros(idx_row.size)
+    grad[ok] = g
+    return loss, grad
+
+
+def indexer_kl(scores, p, q_offset, idx=None):
+    """Per-row losses [B,T] and gradients of the indexer KL objective.
+
+    Dense (idx None): scores and p are [B,T,N]; row t's candidates are
+    s <= q_offset + t; gradients [B,T,N].  Sparse: idx [B,T,k] and p [B,T,k]
+    (the target of each selected slot); gradients [B,T,k]."""
+    scores = np.asarray(scores, dtype=np.float64)
+    B, T, N = scores.shape
+    loss = np.zeros((B, T))
+    if idx is None:
+        grad = np.zeros((B, T, N))
+        for b in range(B):
+            for t in range(T):
+                n_cand = min(N, q_offset + t + 1)
+                loss[b, t], grad[b, t] = indexer_kl_dense_row(scores[b, t], p[b, t], n_cand)
+    else:
+        idx = np.asarray(idx)
+        grad = np.zeros(idx.shape)
+        for b in range(B):
+            for t in range(T):
+                loss[b, t], grad[b, t] = indexer_kl_sparse_row(scores[b, t], idx[b, t], p[b, t])
+    return loss, grad

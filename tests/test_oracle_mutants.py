@@ -11,6 +11,7 @@ import test_oracle_cache as tc
 import test_oracle_forward as tf
 import test_oracle_fp8 as t8
 import test_oracle_indexer as ti
+import test_oracle_kl as tk
 import test_oracle_topk as tt
 
 
@@ -147,3 +148,37 @@ def test_append_position_mutant_caught(monkeypatch, golden_dir):
     monkeypatch.setattr(tc.oracle, "cache_append",
                         lambda k, kv, kc, ks, kvc, pos: orig(k, kv, kc, ks, kvc, np.asarray(pos) + 1))
     assert _fails([tc.test_cache_append_bookkeeping], golden_dir)
+
+
+_ORIG_KL = od._kl_terms
+
+
+def _kl_grad_sign(I, p):
+    loss, g = _ORIG_KL(I, p)
+    return loss, -g
+
+
+def _kl_reversed(I, p):
+    I = np.asarray(I, float)
+    p = np.asarray(p, float)
+    q = np.exp(I - I.max())
+    q /= q.sum()
+    pos = (p > 0) & (q > 0)
+    return float(np.sum(q[pos] * np.log(q[pos] / p[pos]))), q - p
+
+
+def _kl_ignores_causal(I_row, p_row, n_cand):
+    return od._kl_terms(I_row, p_row)
+
+
+@pytest.mark.parametrize("mutant", [_kl_grad_sign, _kl_reversed])
+def test_kl_term_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(od, "_kl_terms", mutant)
+    pins = [tk.test_matches_torch_kl_div_and_autograd, tk.test_one_hot_target_closed_form,
+            tk.test_finite_differences]
+    assert _fails(pins, golden_dir)
+
+
+def test_kl_causal_mutant_caught(monkeypatch, golden_dir):
+    monkeypatch.setattr(tk.oracle, "indexer_kl_dense_row", _kl_ignores_causal)
+    assert _fails([tk.test_causal_range_and_unnormalised_target], golden_dir)
