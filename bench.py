@@ -47,6 +47,7 @@ PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 KERNEL_SOURCES = {"cache_append": ("cache.hip",),
+                  "indexer_kl": ("kl.hip",),
                   "select": ("indexer.hip", "topk.hip", "indexer_math.h", "topk_select.h"),
                   "indexer": ("indexer.hip", "indexer_math.h", "topk_select.h"),
                   "topk": ("topk.hip", "indexer_math.h", "topk_select.h"),
@@ -237,6 +238,35 @@ def time_cache_append(wl, g, steps, stream):
             "algorithmic": nbytes}
 
 
+def time_indexer_kl(wl, scores, idx, steps, stream):
+    """dsa_indexer_kl over the step's [B,T,N] score rows with a random target
+    (dense: HBM-bound, I and p read over the causal candidates, the gradient
+    written over whole rows), then over the k selected slots of each row."""
+    dev = scores.device
+    gen = torch.Generator(device=dev).manual_seed(2)
+    p = torch.rand(scores.shape, generator=gen, device=dev)
+    p /= p.sum(-1, keepdim=True)
+    p_sel = torch.rand(idx.shape, generator=gen, device=dev)
+    p_sel /= p_sel.sum(-1, keepdim=True)
+    out = {}
+    t = np.arange(wl.T, dtype=np.int64)
+    n_cand = int(np.minimum(wl.N, wl.q_offset + t + 1).sum()) * wl.B
+    rows = wl.B * wl.T
+    for name, fn, nbytes in (
+            ("indexer_kl_dense", lambda: dsa.indexer_kl(scores, p, wl.q_offset),
+             8 * n_cand + 4 * rows * wl.N + 4 * rows),
+            ("indexer_kl_sparse", lambda: dsa.indexer_kl(scores, p_sel, idx=idx),
+             16 * rows * wl.k + 4 * rows)):
+        for _ in range(2):
+            fn()
+        ms = timed(fn, steps, stream)
+        ach = nbytes / (ms / 1e3) / 1e9
+        out[name] = {"ms": round(ms, 4), "rows": rows, "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "algorithmic": nbytes}
+    return out
+
+
 def cpu_baseline(wl, g, budget_s):
     """The CPU oracle on a bounded sample of the same workload: whole rows
     (index scores -> selection -> attention), timed on this host's cores."""
@@ -390,6 +420,9 @@ def main():
     # the step before the path (not part of the step): appending this step's
     # new tokens (one per query token) to the key and latent caches
     line["next"] = {"cache_append": time_cache_append(wl, g, args.steps, stream)}
+    # the indexer's alignment objective on this step's score rows (dense
+    # warm-up form) and on its selected slots (sparse form)
+    line["next"].update(time_indexer_kl(wl, scores, idx, args.steps, stream))
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl, g, args.cpu_budget)

@@ -221,6 +221,32 @@ DSA_API dsa_status dsa_cache_append(const float* k_new, const void* kv_new, void
                                     dsa_dtype idx_dtype, dsa_dtype attn_dtype, void* stream);
 
 /*
+ * Indexer alignment objective and its gradient with respect to the index
+ * scores ("Paper Breakdown: DeepSeek-V3.2", section 2, "Continued
+ * Pre-Training (§2.1.1)": the dense warm-up minimises
+ * L^I = sum_t KL(p_t || Softmax(I_t)); sparse training keeps the KL on the
+ * selected set S_t).  For each row b,t, over its entries E (below):
+ *     lse  = log sum_{s in E} exp(I_s)
+ *     loss[b,t] = sum_{s in E, p_s > 0} p_s (log p_s - (I_s - lse))
+ *     grad_s    = P exp(I_s - lse) - p_s,   P = sum_{s in E} p_s
+ * The target is taken as given (a distribution has P = 1; terms with
+ * p_s = 0 vanish).
+ *  Dense (idx == NULL): E = the causal candidates s <= q_offset + t.
+ *    scores [B,T,N] f32, p [B,T,N] f32 (entries outside E are ignored),
+ *    grad [B,T,N] f32 (0 outside E) or NULL; k is ignored.
+ *  Selected set (idx != NULL): E = the slots of idx [B,T,k] int32 whose
+ *    token lies in [0, N) (others are skipped, duplicates count per slot).
+ *    scores [B,T,N] f32, p [B,T,k] f32 = the target of each slot,
+ *    grad [B,T,k] f32 (0 for skipped slots) or NULL; q_offset is ignored.
+ *  loss [B,T] f32.  Scores must be finite or -inf, p finite and >= 0.
+ * fp32 throughout (library expf/logf); a row whose entries are all -inf
+ * gives NaN, as the formula does.
+ */
+DSA_API dsa_status dsa_indexer_kl(const float* scores, const float* p, const int32_t* idx,
+                                  float* loss, float* grad, int B, int T, int N, int k,
+                                  int q_offset, void* stream);
+
+/*
  * Workspace bytes needed by op (a dsa_op) for these sizes; 0 means none.
  * Returns (size_t)-1 for arguments that no call would accept.
  */

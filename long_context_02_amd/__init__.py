@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "DSAError", "lib", "lib_path", "indexer_scores", "topk_select", "sparse_mla_attn",
-    "forward", "indexer_select", "cache_append", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD",
+    "forward", "indexer_select", "cache_append", "indexer_kl", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD",
     "OP_SELECT",
 ]
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_select.restype = ci
     L.dsa_cache_append.argtypes = [fp, vp, vp, fp, vp, i32p, ci, ci, ci, ci, ci, ci, ci, vp]
     L.dsa_cache_append.restype = ci
+    L.dsa_indexer_kl.argtypes = [fp, fp, i32p, fp, fp, ci, ci, ci, ci, ci, vp]
+    L.dsa_indexer_kl.restype = ci
     L.dsa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     L.dsa_workspace_size.restype = sz
     L.dsa_status_string.argtypes = [ci]
@@ -329,3 +331,32 @@ def cache_append(k_new: torch.Tensor, kv_new: torch.Tensor, k_cache: torch.Tenso
         st = lib().dsa_cache_append(_ptr(k_new), _ptr(kv_new), _ptr(_codes(k_cache)), _ptr(k_cache_scale),
                                     _ptr(kv_cache), _ptr(pos), B, T, N, d_I, d_qk, idt, adt, _stream(dev))
     _raise("dsa_cache_append", st)
+
+
+def indexer_kl(scores: torch.Tensor, p: torch.Tensor, q_offset: int = 0,
+               idx: Optional[torch.Tensor] = None, grad: bool = True):
+    """KL(p || softmax(I)) per row and its gradient with respect to the
+    scores: dense over the causal candidates (idx None; p [B,T,N], gradient
+    [B,T,N]) or over the selected slots (idx [B,T,k]; p [B,T,k], gradient
+    [B,T,k]).  Returns (loss [B,T], grad or None)."""
+    dev = scores.device
+    _check("scores", scores, torch.float32, None, dev)
+    B, T, N = scores.shape
+    if idx is None:
+        _check("p", p, torch.float32, (B, T, N), dev)
+        k = 0
+        gshape = (B, T, N)
+    else:
+        _check("idx", idx, torch.int32, None, dev)
+        if idx.dim() != 3 or idx.shape[:2] != (B, T):
+            raise ValueError(f"idx has shape {tuple(idx.shape)}, expected ({B}, {T}, k)")
+        k = idx.shape[2]
+        _check("p", p, torch.float32, (B, T, k), dev)
+        gshape = (B, T, k)
+    loss = torch.empty(B, T, dtype=torch.float32, device=dev)
+    g = torch.empty(gshape, dtype=torch.float32, device=dev) if grad else None
+    with torch.cuda.device(dev):
+        st = lib().dsa_indexer_kl(_ptr(scores), _ptr(p), _ptr(idx), _ptr(loss), _ptr(g), B, T, N, k,
+                                  q_offset, _stream(dev))
+    _raise("dsa_indexer_kl", st)
+    return loss, g

@@ -131,7 +131,7 @@ dsa_status run_attn(const void* q, const void* kv, const int32_t* idx, void* out
 
 extern "C" {
 
-int dsa_version(void) { return (1 << 16) | 1; }
+int dsa_version(void) { return (1 << 16) | 2; }
 
 const char* dsa_status_string(dsa_status s) {
     switch (s) {
@@ -278,6 +278,25 @@ dsa_status dsa_cache_append(const float* k_new, const void* kv_new, void* k_cach
     }
     return launch_cache_append(k_new, kv_new, k_cache, k_cache_scale, kv_cache, pos, B, T, N, d_I,
                                row_bytes, fp8, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_indexer_kl(const float* scores, const float* p, const int32_t* idx, float* loss,
+                          float* grad, int B, int T, int N, int k, int q_offset, void* stream) {
+    if (!scores || !p || !loss) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(scores) || !aligned16(p) || !aligned16(loss) || (grad && !aligned16(grad)) ||
+        (idx && !aligned16(idx)))
+        return DSA_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || N < 1) return DSA_ERR_INVALID_ARG;
+    if ((long long)B * T >= (1LL << 31) || (long long)B * T * (long long)N >= (1LL << 40))
+        return DSA_ERR_UNSUPPORTED;
+    if (idx) {
+        if (k < 1) return DSA_ERR_INVALID_ARG;
+        if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+    } else {
+        if (q_offset < 0 || (long long)q_offset + T > N) return DSA_ERR_INVALID_ARG;
+    }
+    return launch_indexer_kl(scores, p, idx, loss, grad, B, T, N, k, q_offset,
+                             static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -99,6 +99,13 @@ dsa_status launch_cache_append(const float* k_new, const void* kv_new, void* k_c
                                void* kv_cache, const int32_t* pos, int B, int T, int N, int d_i,
                                int kv_row_bytes, bool fp8, hipStream_t stream);
 
+// ---- indexer KL objective (kl.hip) -----------------------------------------
+// idx == nullptr: dense rows (p, grad [B,T,N], causal range from q_offset);
+// otherwise the k selected slots of each row (p, grad [B,T,k]).  grad may be
+// nullptr.
+dsa_status launch_indexer_kl(const float* scores, const float* p, const int32_t* idx, float* loss,
+                             float* grad, int B, int T, int N, int k, int q_offset, hipStream_t stream);
+
 inline dsa_status launch_status() {
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

@@ -1,0 +1,169 @@
+// Indexer alignment objective on gfx950 ("Paper Breakdown: DeepSeek-V3.2",
+// section 2, "Continued Pre-Training (§2.1.1)"): the dense warm-up trains the
+// indexer with L^I = sum_t KL(p_t || Softmax(I_t)), sparse training keeps the
+// KL on the selected set S_t.  Per row, over the row's entries (the causal
+// candidates s <= q_offset + t, or the valid selected slots):
+//     lse  = log sum_s exp(I_s)
+//     loss = sum_{p_s > 0} p_s (log p_s - (I_s - lse))
+//     dL/dI_s = P exp(I_s - lse) - p_s,   P = sum_s p_s
+// (the target is taken as given; for a distribution P = 1).
+//
+// Dense: one 1024-thread workgroup per row, two passes over the row.  Pass 1
+// streams I and p once for the running max / exp-sum (lse) and P; pass 2
+// streams them again for the loss terms and writes the gradient (zeros past
+// the causal range).  HBM-bound: 16 B read and 4 B written per candidate.
+// Sparse: one 256-thread workgroup per row gathers the k selected scores.
+// Everything in fp32 with the library expf / logf.
+#include <cmath>
+
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int KT = 1024;   // dense: threads per row
+constexpr int ST = 256;    // sparse: threads per row
+
+struct Acc {
+    float m;  // running max
+    float l;  // sum exp(I - m)
+};
+
+__device__ __forceinline__ Acc acc_merge(Acc a, Acc b) {
+    const float m = fmaxf(a.m, b.m);
+    if (m == -__builtin_inff()) return Acc{m, 0.f};
+    return Acc{m, a.l * expf(a.m - m) + b.l * expf(b.m - m)};
+}
+
+// add exp(x) to the running sum; x = -inf adds nothing (scores are finite
+// or -inf)
+__device__ __forceinline__ Acc acc_add(Acc a, float x) {
+    if (x == -__builtin_inff()) return a;
+    if (x <= a.m) return Acc{a.m, a.l + expf(x - a.m)};
+    return Acc{x, a.l * expf(a.m - x) + 1.f};  // new max (from -inf: a.l = 0)
+}
+
+// Block-wide reductions (NTH threads, shared scratch of NTH/64 entries).
+template <int NTH>
+__device__ __forceinline__ Acc block_acc(Acc a, Acc* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        Acc o{__shfl_xor(a.m, off, 64), __shfl_xor(a.l, off, 64)};
+        a = acc_merge(a, o);
+    }
+    __syncthreads();
+    if (lane == 0) sh[w] = a;
+    __syncthreads();
+    Acc r = sh[0];
+    for (int i = 1; i < NTH / 64; ++i) r = acc_merge(r, sh[i]);
+    return r;
+}
+
+template <int NTH>
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if (lane == 0) sh[w] = v;
+    __syncthreads();
+    float r = 0.f;
+    for (int i = 0; i < NTH / 64; ++i) r += sh[i];
+    return r;
+}
+
+__device__ __forceinline__ float kl_term(float pv, float d) {  // p (log p - d), 0 for p = 0
+    return pv > 0.f ? pv * (logf(pv) - d) : 0.f;
+}
+
+__global__ __launch_bounds__(KT) void indexer_kl_dense(const float* __restrict__ scores,
+                                                       const float* __restrict__ p,
+                                                       float* __restrict__ loss, float* __restrict__ grad,
+                                                       int T, int N, int q_offset) {
+    __shared__ Acc sh_acc[KT / 64];
+    __shared__ float sh_f[KT / 64];
+    const size_t row = blockIdx.x;
+    const int t = (int)(row % (size_t)T);
+    const int n = (int)min((long long)N, (long long)q_offset + t + 1);
+    const float* __restrict__ I = scores + row * N;
+    const float* __restrict__ pr = p + row * N;
+
+    Acc a{-__builtin_inff(), 0.f};
+    float P = 0.f;
+    for (int s = threadIdx.x; s < n; s += KT) {
+        a = acc_add(a, I[s]);
+        P += pr[s];
+    }
+    a = block_acc<KT>(a, sh_acc);
+    P = block_sum<KT>(P, sh_f);
+    const float lse = a.m + logf(a.l);
+
+    float L = 0.f;
+    for (int s = threadIdx.x; s < N; s += KT) {
+        if (s < n) {
+            const float d = I[s] - lse;
+            const float pv = pr[s];
+            L += kl_term(pv, d);
+            if (grad) grad[row * N + s] = P * expf(d) - pv;
+        } else if (grad) {
+            grad[row * N + s] = 0.f;
+        }
+    }
+    L = block_sum<KT>(L, sh_f);
+    if (threadIdx.x == 0) loss[row] = L;
+}
+
+__global__ __launch_bounds__(ST) void indexer_kl_sparse(const float* __restrict__ scores,
+                                                        const float* __restrict__ p_sel,
+                                                        const int32_t* __restrict__ idx,
+                                                        float* __restrict__ loss,
+                                                        float* __restrict__ grad, int N, int k) {
+    __shared__ Acc sh_acc[ST / 64];
+    __shared__ float sh_f[ST / 64];
+    const size_t row = blockIdx.x;
+    const float* __restrict__ I = scores + row * N;
+    const int32_t* __restrict__ ir = idx + row * k;
+    const float* __restrict__ pr = p_sel + row * k;
+
+    Acc a{-__builtin_inff(), 0.f};
+    float P = 0.f;
+    for (int i = threadIdx.x; i < k; i += ST) {
+        const int s = ir[i];
+        if (s < 0 || s >= N) continue;
+        a = acc_add(a, I[s]);
+        P += pr[i];
+    }
+    a = block_acc<ST>(a, sh_acc);
+    P = block_sum<ST>(P, sh_f);
+    const float lse = a.m + logf(a.l);
+
+    float L = 0.f;
+    for (int i = threadIdx.x; i < k; i += ST) {
+        const int s = ir[i];
+        float g = 0.f;
+        if (s >= 0 && s < N) {
+            const float d = I[s] - lse;
+            const float pv = pr[i];
+            L += kl_term(pv, d);
+            g = P * expf(d) - pv;
+        }
+        if (grad) grad[row * k + i] = g;
+    }
+    L = block_sum<ST>(L, sh_f);
+    if (threadIdx.x == 0) loss[row] = L;
+}
+
+}  // namespace
+
+dsa_status launch_indexer_kl(const float* scores, const float* p, const int32_t* idx, float* loss,
+                             float* grad, int B, int T, int N, int k, int q_offset, hipStream_t stream) {
+    const unsigned rows = (unsigned)((long long)B * T);
+    if (idx == nullptr)
+        indexer_kl_dense<<<rows, KT, 0, stream>>>(scores, p, loss, grad, T, N, q_offset);
+    else
+        indexer_kl_sparse<<<rows, ST, 0, stream>>>(scores, p, idx, loss, grad, N, k);
+    return launch_status();
+}
+
+}  // namespace dsa

@@ -153,3 +153,18 @@ def test_cache_append_rejects_bad_arguments():
     assert call(adt=dsa.F32, d_qk=300) == 2
     assert call(idt=dsa.BF16) == 2 and call(adt=dsa.FP8_E4M3FN) == 2
     assert call(B=0) == 1 and call(T=0) == 1
+
+
+def test_indexer_kl_rejects_bad_arguments():
+    f = dsa.lib().dsa_indexer_kl
+
+    def call(ptrs=None, B=1, T=4, N=8, k=0, q_offset=4):
+        ptrs = ptrs or [P, P, None, P, P]
+        return f(*ptrs, B, T, N, k, q_offset, None)
+
+    assert call(ptrs=[None, P, None, P, P]) == 1
+    assert call(ptrs=[P, P, None, None, P]) == 1          # loss is required
+    assert call(q_offset=5) == 1                          # dense: q_offset + T > N
+    assert call(ptrs=[P, P, P, P, None], k=0) == 1        # selected slots need k >= 1
+    assert call(ptrs=[P, P, P, P, None], k=4096) == 2
+    assert call(B=0) == 1

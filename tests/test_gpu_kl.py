@@ -1,0 +1,140 @@
+"""GPU parity of dsa_indexer_kl (dense warm-up and selected-set forms)
+against the oracle's float64 loss and gradient.
+
+Tolerance, from fp32 arithmetic: the log-sum-exp is a sum of at most ~128
+terms per thread plus a tree, so its error is below 2^-16 + |lse| 2^-22 (the
+last term for rounding lse itself); each loss term p (log p - d) carries
+that error times p plus a few roundings of its own, and each gradient
+P exp(d) - p the relative error of exp(d), i.e. the error of d:
+    |dL| <= P (2^-16 + |lse| 2^-22) + 2^-16 sum p (|log p| + |d|)
+    |dg| <= P q (2^-16 + (|lse| + |d|) 2^-21) + 2^-22 (P q + p)
+with d = I - lse and q = exp(d) from the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_02_amd as dsa
+import oracle
+from dsa_parity import gpu_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _stats(I, p):
+    I = np.asarray(I, np.float64)
+    p = np.asarray(p, np.float64)
+    m = np.max(I)
+    lse = m + np.log(np.sum(np.exp(I - m)))
+    d = I - lse
+    q = np.exp(d)
+    P = p.sum()
+    with np.errstate(divide="ignore"):
+        lp = np.where(p > 0, np.abs(np.log(np.where(p > 0, p, 1.0))), 0.0)
+    fin = np.isfinite(d)
+    tol_l = P * (2.0 ** -16 + abs(lse) * 2.0 ** -22) + 2.0 ** -16 * np.sum(p * lp + np.where(fin, p * np.abs(d), 0))
+    tol_g = P * q * (2.0 ** -16 + (abs(lse) + np.where(fin, np.abs(d), 0)) * 2.0 ** -21) + 2.0 ** -22 * (P * q + p)
+    return tol_l, tol_g
+
+
+def _check_row(where, gl, gg, I, p, ref_l, ref_g):
+    tol_l, tol_g = _stats(I, p)
+    assert abs(gl - ref_l) <= tol_l, f"{where}: loss {gl} vs {ref_l} (tol {tol_l:.3e})"
+    err = np.abs(gg - ref_g)
+    bad = np.flatnonzero(err > tol_g)
+    assert bad.size == 0, f"{where}: {bad.size} gradient entries off, first {bad[0]}: {gg[bad[0]]} vs {ref_g[bad[0]]}"
+
+
+def _target(I, gen, zeros=0.2):
+    """A target distribution like an attention row: softmax of a noisy copy
+    of the scores, with some exact zeros."""
+    x = torch.nan_to_num(I, neginf=-1e30) * 0.7 + torch.randn(I.shape, generator=gen) * 2
+    p = torch.softmax(x, dim=-1)
+    p = torch.where(torch.rand(I.shape, generator=gen) < zeros, torch.zeros_like(p), p)
+    return p / p.sum(-1, keepdim=True).clamp_min(1e-30)
+
+
+@pytest.mark.parametrize("B,T,N,q_offset", [
+    (2, 40, 3000, 2960),    # chunk-like rows, several thread strides, ragged N
+    (1, 300, 300, 0),       # prefill: rows of 1..300 candidates
+    (3, 1, 5000, 4999),     # decode rows
+])
+def test_dense_rows(B, T, N, q_offset):
+    dev = gpu_device()
+    gen = torch.Generator().manual_seed(N + T)
+    I = torch.randn(B, T, N, generator=gen) * 4
+    I[:, :, ::97] = -float("inf")             # masked entries inside the causal range
+    I[..., 0] = torch.randn(B, T, generator=gen)  # every row keeps a finite entry
+    p = _target(I, gen)
+    p = torch.where(torch.isinf(I), torch.zeros_like(p), p)
+    print(f"[kl] dense B={B} T={T} N={N}", flush=True)
+    loss, grad = dsa.indexer_kl(I.to(dev), p.to(dev).contiguous(), q_offset)
+    torch.cuda.synchronize()
+    gl, gg = loss.cpu().numpy(), grad.cpu().numpy()
+    ref_l, ref_g = oracle.indexer_kl(I.numpy(), p.numpy(), q_offset)
+    for b in range(B):
+        for t in range(T):
+            n = min(N, q_offset + t + 1)
+            _check_row(f"dense b={b} t={t}", gl[b, t], gg[b, t, :n], I[b, t, :n].numpy(), p[b, t, :n].numpy(),
+                       ref_l[b, t], ref_g[b, t, :n])
+            assert np.all(gg[b, t, n:] == 0)
+
+
+def test_selected_slots():
+    dev = gpu_device()
+    gen = torch.Generator().manual_seed(21)
+    B, T, N, k = 2, 6, 6000, 2048
+    I = torch.randn(B, T, N, generator=gen) * 3
+    idx = torch.stack([torch.randperm(N, generator=gen)[:k] for _ in range(B * T)]).view(B, T, k).int()
+    idx[0, 1, 1500:] = -1                      # padded row
+    idx[1, 2, 10] = idx[1, 2, 11]              # a duplicate
+    idx[1, 3, 5] = N + 3                       # out of range: skipped
+    p = torch.rand(B, T, k, generator=gen)
+    p[idx < 0] = 0.0
+    p = p / p.sum(-1, keepdim=True)
+    print("[kl] selected slots", flush=True)
+    loss, grad = dsa.indexer_kl(I.to(dev), p.to(dev), idx=idx.to(dev))
+    torch.cuda.synchronize()
+    gl, gg = loss.cpu().numpy(), grad.cpu().numpy()
+    ref_l, ref_g = oracle.indexer_kl(I.numpy(), p.numpy(), 0, idx=idx.numpy())
+    for b in range(B):
+        for t in range(T):
+            ok = (idx[b, t] >= 0) & (idx[b, t] < N)
+            sel = idx[b, t][ok].long()
+            _check_row(f"sparse b={b} t={t}", gl[b, t], gg[b, t][ok.numpy()], I[b, t][sel].numpy(),
+                       p[b, t][ok].numpy(), ref_l[b, t], ref_g[b, t][ok.numpy()])
+            assert np.all(gg[b, t][~ok.numpy()] == 0)
+
+
+def test_loss_only_and_zero_target():
+    dev = gpu_device()
+    gen = torch.Generator().manual_seed(22)
+    I = torch.randn(1, 4, 700, generator=gen)
+    p = torch.zeros(1, 4, 700)
+    p[0, 1, 3] = 1.0                           # one-hot
+    loss, grad = dsa.indexer_kl(I.to(dev), p.to(dev), 696, grad=False)
+    torch.cuda.synchronize()
+    assert grad is None
+    ref_l, _ = oracle.indexer_kl(I.numpy(), p.numpy(), 696)
+    assert loss[0, 0].item() == 0.0 and loss[0, 2].item() == 0.0   # zero target
+    assert abs(loss[0, 1].item() - ref_l[0, 1]) < 1e-5
+
+
+def test_chunk_sized_rows_sampled():
+    """4096 rows of 131072 candidates (the chunked-prefill score matrix
+    shape, one workgroup per row as bench.py runs it); sampled rows against
+    the oracle."""
+    dev = gpu_device()
+    T, N, q_off = 4096, 131072, 126976
+    g = torch.Generator(device=dev).manual_seed(23)
+    I = torch.randn(1, T, N, generator=g, device=dev) * 5
+    p = torch.softmax(I * 0.5 + torch.randn(1, T, N, generator=g, device=dev), dim=-1)
+    print("[kl] chunk-sized rows", flush=True)
+    loss, grad = dsa.indexer_kl(I, p, q_off)
+    torch.cuda.synchronize()
+    for t in (0, 1, 777, 2048, 4095):
+        n = q_off + t + 1
+        It, pt = I[0, t].cpu().numpy(), p[0, t].cpu().numpy()
+        ref_l, ref_g = oracle.indexer_kl_dense_row(It, pt, n)
+        gg = grad[0, t].cpu().numpy()
+        _check_row(f"chunk t={t}", loss[0, t].item(), gg[:n], It[:n], pt[:n], ref_l, ref_g[:n])
+        assert np.all(gg[n:] == 0)
