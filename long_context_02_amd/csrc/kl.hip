@@ -77,6 +77,18 @@ __device__ __forceinline__ float kl_term(float pv, float d) {  // p (log p - d),
     return pv > 0.f ? pv * (logf(pv) - d) : 0.f;
 }
 
+// four consecutive entries at once; entries equal to -inf add nothing
+__device__ __forceinline__ Acc acc_add4(Acc a, const float4& x) {
+    const float m4 = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+    if (m4 == -__builtin_inff()) return a;
+    if (m4 > a.m) {
+        a.l *= expf(a.m - m4);  // from -inf: a.l = 0
+        a.m = m4;
+    }
+    a.l += expf(x.x - a.m) + expf(x.y - a.m) + expf(x.z - a.m) + expf(x.w - a.m);
+    return a;
+}
+
 __global__ __launch_bounds__(KT) void indexer_kl_dense(const float* __restrict__ scores,
                                                        const float* __restrict__ p,
                                                        float* __restrict__ loss, float* __restrict__ grad,
@@ -88,10 +100,22 @@ __global__ __launch_bounds__(KT) void indexer_kl_dense(const float* __restrict__
     const int n = (int)min((long long)N, (long long)q_offset + t + 1);
     const float* __restrict__ I = scores + row * N;
     const float* __restrict__ pr = p + row * N;
+    float* __restrict__ gr = grad ? grad + row * N : nullptr;
+    // rows of a multiple of 4 entries are 16-byte aligned: whole float4s over
+    // [0, 4*n4), single entries over the rest
+    const bool vec = (N & 3) == 0;
+    const int n4 = vec ? n >> 2 : 0;
 
     Acc a{-__builtin_inff(), 0.f};
     float P = 0.f;
-    for (int s = threadIdx.x; s < n; s += KT) {
+#pragma unroll 2
+    for (int j = threadIdx.x; j < n4; j += KT) {
+        const float4 x = reinterpret_cast<const float4*>(I)[j];
+        const float4 pv = reinterpret_cast<const float4*>(pr)[j];
+        a = acc_add4(a, x);
+        P += (pv.x + pv.y) + (pv.z + pv.w);
+    }
+    for (int s = 4 * n4 + threadIdx.x; s < n; s += KT) {
         a = acc_add(a, I[s]);
         P += pr[s];
     }
@@ -100,15 +124,30 @@ __global__ __launch_bounds__(KT) void indexer_kl_dense(const float* __restrict__
     const float lse = a.m + logf(a.l);
 
     float L = 0.f;
-    for (int s = threadIdx.x; s < N; s += KT) {
-        if (s < n) {
-            const float d = I[s] - lse;
-            const float pv = pr[s];
-            L += kl_term(pv, d);
-            if (grad) grad[row * N + s] = P * expf(d) - pv;
-        } else if (grad) {
-            grad[row * N + s] = 0.f;
-        }
+#pragma unroll 2
+    for (int j = threadIdx.x; j < n4; j += KT) {
+        const float4 x = reinterpret_cast<const float4*>(I)[j];
+        const float4 pv = reinterpret_cast<const float4*>(pr)[j];
+        const float4 d = {x.x - lse, x.y - lse, x.z - lse, x.w - lse};
+        L += (kl_term(pv.x, d.x) + kl_term(pv.y, d.y)) + (kl_term(pv.z, d.z) + kl_term(pv.w, d.w));
+        if (gr)
+            reinterpret_cast<float4*>(gr)[j] =
+                float4{P * expf(d.x) - pv.x, P * expf(d.y) - pv.y, P * expf(d.z) - pv.z, P * expf(d.w) - pv.w};
+    }
+    for (int s = 4 * n4 + threadIdx.x; s < n; s += KT) {
+        const float d = I[s] - lse;
+        const float pv = pr[s];
+        L += kl_term(pv, d);
+        if (gr) gr[s] = P * expf(d) - pv;
+    }
+    if (gr) {  // zeros past the causal range
+        const int z0 = (n + 3) & ~3;
+        for (int s = n + threadIdx.x; s < min(z0, N); s += KT) gr[s] = 0.f;
+        if (vec)
+            for (int j = (z0 >> 2) + threadIdx.x; j < (N >> 2); j += KT)
+                reinterpret_cast<float4*>(gr)[j] = float4{0.f, 0.f, 0.f, 0.f};
+        else
+            for (int s = z0 + threadIdx.x; s < N; s += KT) gr[s] = 0.f;
     }
     L = block_sum<KT>(L, sh_f);
     if (threadIdx.x == 0) loss[row] = L;
@@ -121,34 +160,45 @@ __global__ __launch_bounds__(ST) void indexer_kl_sparse(const float* __restrict_
                                                         float* __restrict__ grad, int N, int k) {
     __shared__ Acc sh_acc[ST / 64];
     __shared__ float sh_f[ST / 64];
+    constexpr int PER = 8;  // slots per thread and round (k <= 2048 = ST * PER)
     const size_t row = blockIdx.x;
     const float* __restrict__ I = scores + row * N;
     const int32_t* __restrict__ ir = idx + row * k;
     const float* __restrict__ pr = p_sel + row * k;
 
+    // every slot this thread owns: index, target and score, loads issued together
+    float xs[PER], ps[PER];
+    bool ok[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = threadIdx.x + u * ST;
+        const int s = i < k ? ir[i] : -1;
+        ok[u] = s >= 0 && s < N;
+        ps[u] = ok[u] ? pr[i] : 0.f;
+        xs[u] = ok[u] ? I[s] : -__builtin_inff();
+    }
     Acc a{-__builtin_inff(), 0.f};
     float P = 0.f;
-    for (int i = threadIdx.x; i < k; i += ST) {
-        const int s = ir[i];
-        if (s < 0 || s >= N) continue;
-        a = acc_add(a, I[s]);
-        P += pr[i];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        a = acc_add(a, xs[u]);
+        P += ps[u];
     }
     a = block_acc<ST>(a, sh_acc);
     P = block_sum<ST>(P, sh_f);
     const float lse = a.m + logf(a.l);
 
     float L = 0.f;
-    for (int i = threadIdx.x; i < k; i += ST) {
-        const int s = ir[i];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = threadIdx.x + u * ST;
         float g = 0.f;
-        if (s >= 0 && s < N) {
-            const float d = I[s] - lse;
-            const float pv = pr[i];
-            L += kl_term(pv, d);
-            g = P * expf(d) - pv;
+        if (ok[u]) {
+            const float d = xs[u] - lse;
+            L += kl_term(ps[u], d);
+            g = P * expf(d) - ps[u];
         }
-        if (grad) grad[row * k + i] = g;
+        if (grad && i < k) grad[row * k + i] = g;
     }
     L = block_sum<ST>(L, sh_f);
     if (threadIdx.x == 0) loss[row] = L;
