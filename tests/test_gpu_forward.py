@@ -106,7 +106,9 @@ def test_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("name,B,T", [("decode_128k", 64, 1), ("decode_128k", 4, 2),
-                                      ("chunk_128k", 2, 7), ("prefill_8k", 1, 300)])
+                                      ("chunk_128k", 2, 7), ("prefill_8k", 1, 300),
+                                      ("chunk_128k", 1, 40), ("chunk_128k", 2, 200),
+                                      ("chunk_128k", 1, 4096)])
 def test_forward_selection_matches_separate_calls(name, B, T):
     """The selection inside dsa_forward (and dsa_indexer_select) equals, bit
     for bit, dsa_topk_select run on dsa_indexer_scores' output: candidate
