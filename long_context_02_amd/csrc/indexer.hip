@@ -21,6 +21,8 @@
 //  * indexer_fp8_stream (T < 16, e.g. decode): the key stream is read once,
 //    so each wave loads its 16-key fragments straight from HBM (see the
 //    kernel for its own MFMA row layout and store pattern).
+#include <type_traits>
+
 #include "indexer_math.h"
 #include "topk_select.h"
 
@@ -129,27 +131,33 @@ __global__ __launch_bounds__(NTT) void indexer_fp8_tiled(
                 // a clean tile: every key visible to all of the wave's queries, all in range
                 const bool clean = vec_out && s0 + TILE - 1 <= q_offset + tw0 && tw0 + QPW <= T &&
                                    s0 + TILE <= s_end;
+                // the scores of the tile into LDS; the causal mask only on the
+                // tiles that need it (two copies of the loop)
+                auto scores16 = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-                for (int sub = 0; sub < TILE / 16; ++sub) {
-                    const int key = 16 * sub + m;
-                    const uint8_t* src = &lds_k[buf][key * ROWB + 32 * kb];
-                    const i32x8 bf = pack8(*reinterpret_cast<const uint4*>(src),
-                                           *reinterpret_cast<const uint4*>(src + 16));
-                    const float ksc = lds_ks[buf][key];
-                    const int s_abs = s0 + key;
-                    f32x4 acc[GPW][2];
+                    for (int sub = 0; sub < TILE / 16; ++sub) {
+                        const int key = 16 * sub + m;
+                        const uint8_t* src = &lds_k[buf][key * ROWB + 32 * kb];
+                        const i32x8 bf = pack8(*reinterpret_cast<const uint4*>(src),
+                                               *reinterpret_cast<const uint4*>(src + 16));
+                        const float ksc = lds_ks[buf][key];
+                        f32x4 acc[GPW][2];
 #pragma unroll
-                    for (int g = 0; g < GPW; ++g) {
-                        acc[g][0] = mfma_fp8(a[g][0], bf);
-                        acc[g][1] = mfma_fp8(a[g][1], bf);
+                        for (int g = 0; g < GPW; ++g) {
+                            acc[g][0] = mfma_fp8(a[g][0], bf);
+                            acc[g][1] = mfma_fp8(a[g][1], bf);
+                        }
+#pragma unroll
+                        for (int g = 0; g < GPW; ++g) {
+                            float sc = head_sum(acc[g][0], acc[g][1], ws[g]) * ksc;
+                            if (decltype(masked)::value && s0 + key > q_offset + tw0 + 4 * g + kb)
+                                sc = -__builtin_inff();
+                            ost[(4 * g + kb) * OST + key] = sc;
+                        }
                     }
-#pragma unroll
-                    for (int g = 0; g < GPW; ++g) {
-                        float sc = head_sum(acc[g][0], acc[g][1], ws[g]) * ksc;
-                        if (!clean && s_abs > q_offset + tw0 + 4 * g + kb) sc = -__builtin_inff();
-                        ost[(4 * g + kb) * OST + key] = sc;
-                    }
-                }
+                };
+                if (clean) scores16(std::false_type{});
+                else scores16(std::true_type{});
                 // QPW rows x 64 keys out of LDS: lane l takes 16 bytes of row
                 // 4j + l/16 per step, each row a whole 256-byte segment
                 const int c = lane & 15;
