@@ -23,6 +23,10 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
   sparse_mqa_attention            pinned (k >= L equals dense causal attention
                                   from torch SDPA; q = 0 mean; single index;
                                   permutation and duplicate closed forms)
+  sparse_mqa_attention_bwd        pinned (central finite differences of the
+                                  forward, float64 autograd through torch
+                                  SDPA when k >= L, gradient sums
+                                  sum_h dq.q = sum_i dc_i.c_i, duplicates)
   dsa_forward                     pinned (composition; chunked prefill equals
                                   the tail rows of a full prefill)
 """
@@ -34,6 +38,8 @@ from .dsa import (  # noqa: F401
     topk_select_row,
     sparse_mqa_attention,
     sparse_mqa_attention_row,
+    sparse_mqa_attention_bwd,
+    sparse_mqa_attention_bwd_row,
     dsa_forward,
     default_sm_scale,
     cache_append,

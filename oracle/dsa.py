@@ -218,6 +218,75 @@ def sparse_mqa_attention(q, kv, idx, d_v, sm_scale, rows=None):
 
 
 # --------------------------------------------------------------------------
+# Sparse attention backward (the sparse training stage)
+# --------------------------------------------------------------------------
+# "Paper Breakdown: DeepSeek-V3.2", section 2, "Continued Pre-Training
+# (§2.1.1)": in the sparse training stage the main model is trained through
+# the sparse attention (only the selected entries c_s take part), so the
+# gradients of u_t = Attn(h_t, {c_s : selected}) with respect to the query
+# heads and to the selected latent entries are needed.  They follow from the
+# chain rule through the forward above; with z[h,i] = scale * q[h] . c_i,
+# P = softmax_i(z[h,:]) over the valid slots and o[h] = sum_i P[h,i] c_i[:d_v]:
+#     dP[h,i] = do[h] . c_i[:d_v]
+#     dz[h,i] = P[h,i] * (dP[h,i] - sum_j P[h,j] dP[h,j])
+#     dq[h]   = scale * sum_i dz[h,i] c_i
+#     dc_i    = scale * sum_h dz[h,i] q[h]  (+ sum_h P[h,i] do[h] on [:d_v])
+# A slot outside [0, N) contributes nothing; a token selected in several
+# slots receives the sum of their contributions.
+
+def sparse_mqa_attention_bwd_row(q_row, kv, idx_row, do_row, d_v, sm_scale):
+    """Gradients of one query token's sparse MQA attention.
+
+    q_row [H, d_qk], kv [N, d_qk], idx_row [k], do_row [H, d_v] (the
+    gradient of the loss with respect to the row's output o).  Returns
+    (dq [H, d_qk], dkv [N, d_qk]) in float64; dkv is zero outside the
+    selected rows.
+    """
+    N = kv.shape[0]
+    q_row = np.asarray(q_row, dtype=np.float64)
+    do_row = np.asarray(do_row, dtype=np.float64)
+    idx_row = np.asarray(idx_row)
+    sel = idx_row[(idx_row >= 0) & (idx_row < N)]
+    H, d_qk = q_row.shape
+    dkv = np.zeros((N, d_qk))
+    if sel.size == 0:
+        return np.zeros((H, d_qk)), dkv
+    C = np.asarray(kv[sel], dtype=np.float64)         # [k', d_qk]
+    z = sm_scale * (q_row @ C.T)                      # [H, k']
+    P = np.exp(z - z.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    dP = do_row @ C[:, :d_v].T                        # [H, k']
+    dz = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+    dq = sm_scale * (dz @ C)
+    dC = sm_scale * (dz.T @ q_row)                    # [k', d_qk]
+    dC[:, :d_v] += P.T @ do_row
+    np.add.at(dkv, sel, dC)
+    return dq, dkv
+
+
+def sparse_mqa_attention_bwd(q, kv, idx, do, d_v, sm_scale):
+    """Gradients of sparse MQA attention for a whole batch.
+
+    q [B,T,H,d_qk], kv [B,N,d_qk], idx [B,T,k], do [B,T,H,d_v].  Returns
+    (dq [B,T,H,d_qk], dkv [B,N,d_qk]) in float64; dkv sums the contributions
+    of every query row of the sequence.
+    """
+    q = np.asarray(q)
+    kv = np.asarray(kv)
+    idx = np.asarray(idx)
+    do = np.asarray(do)
+    B, T, H, d_qk = q.shape
+    dq = np.zeros((B, T, H, d_qk))
+    dkv = np.zeros((B, kv.shape[1], d_qk))
+    for b in range(B):
+        for t in range(T):
+            dq[b, t], g = sparse_mqa_attention_bwd_row(q[b, t], kv[b], idx[b, t], do[b, t],
+                                                       d_v, sm_scale)
+            dkv[b] += g
+    return dq, dkv
+
+
+# --------------------------------------------------------------------------
 # The whole path
 
 

@@ -182,3 +182,50 @@ def test_kl_term_mutants_caught(monkeypatch, golden_dir, mutant):
 def test_kl_causal_mutant_caught(monkeypatch, golden_dir):
     monkeypatch.setattr(tk.oracle, "indexer_kl_dense_row", _kl_ignores_causal)
     assert _fails([tk.test_causal_range_and_unnormalised_target], golden_dir)
+
+
+# ---- sparse attention backward
+import test_oracle_attn_bwd as tb  # noqa: E402
+
+BWD_PINS = [tb.test_central_finite_differences, tb.test_k_ge_L_equals_torch_autograd_of_dense_causal,
+            tb.test_query_and_latent_gradients_identity, tb.test_one_distinct_token_closed_form]
+
+
+def _bwd_variant(drop_value=False, no_centre=False, dq_unscaled=False, dkv_from_do=False,
+                 dup_once=False, centre_sign=1.0):
+    def row(q_row, kv, idx_row, do_row, d_v, sm_scale):
+        N = kv.shape[0]
+        idx_row = np.asarray(idx_row)
+        sel = idx_row[(idx_row >= 0) & (idx_row < N)]
+        H, d_qk = q_row.shape
+        dkv = np.zeros((N, d_qk))
+        if sel.size == 0:
+            return np.zeros((H, d_qk)), dkv
+        C = np.asarray(kv[sel], dtype=np.float64)
+        z = sm_scale * (q_row @ C.T)
+        P = np.exp(z - z.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dP = do_row @ C[:, :d_v].T
+        D = np.sum(P * dP, axis=1, keepdims=True)
+        dz = P * dP if no_centre else P * (dP - centre_sign * D)
+        dq = (1.0 if dq_unscaled else sm_scale) * (dz @ C)
+        src = np.concatenate([do_row, q_row[:, d_v:]], axis=1) if dkv_from_do else q_row
+        dC = sm_scale * (dz.T @ src)
+        if not drop_value:
+            dC[:, :d_v] += P.T @ do_row
+        if dup_once:
+            dkv[sel] = dC
+        else:
+            np.add.at(dkv, sel, dC)
+        return dq, dkv
+    return row
+
+
+@pytest.mark.parametrize("kw", [dict(drop_value=True), dict(no_centre=True), dict(dq_unscaled=True),
+                                dict(dkv_from_do=True), dict(dup_once=True), dict(centre_sign=-1.0)])
+def test_attention_bwd_mutants_caught(monkeypatch, golden_dir, kw):
+    # the unmodified variant passes every pin
+    monkeypatch.setattr(od, "sparse_mqa_attention_bwd_row", _bwd_variant())
+    assert not _fails(BWD_PINS, golden_dir)
+    monkeypatch.setattr(od, "sparse_mqa_attention_bwd_row", _bwd_variant(**kw))
+    assert _fails(BWD_PINS, golden_dir)
