@@ -47,11 +47,12 @@ PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 KERNEL_SOURCES = {"cache_append": ("cache.hip",),
+                  "attn_bwd": ("attention_bwd.hip", "attn_common.h"),
                   "indexer_kl": ("kl.hip",),
                   "select": ("indexer.hip", "topk.hip", "indexer_math.h", "topk_select.h"),
                   "indexer": ("indexer.hip", "indexer_math.h", "topk_select.h"),
                   "topk": ("topk.hip", "indexer_math.h", "topk_select.h"),
-                  "attention": ("attention.hip",)}
+                  "attention": ("attention.hip", "attn_common.h")}
 
 
 def source_hash(phase):
@@ -267,6 +268,43 @@ def time_indexer_kl(wl, scores, idx, steps, stream):
     return out
 
 
+def time_attn_bwd(wl, g, idx, steps, stream):
+    """dsa_sparse_mla_attn_bwd on the step's selection with a random output
+    gradient (the sparse training stage's attention backward).  Algorithmic
+    work per valid slot and head: 2 x (576 + 512) FLOP to recompute the logit
+    and form dP, 2 x 576 for dq, 2 x (576 + 512) for the latent gradient;
+    bytes: q, out, dout and lse read, dq written, the selected latent rows
+    gathered once, dkv written once."""
+    dev = g["q"].device
+    B, T, N = wl.B, wl.T, wl.N
+    out, lse = dsa.sparse_mla_attn(g["q"], g["kv"], idx, wl.d_v, wl.sm_scale)
+    gen = torch.Generator(device=dev).manual_seed(3)
+    dout = torch.randn(out.shape, generator=gen, device=dev, dtype=out.dtype)
+    dq = torch.empty(B, T, wl.H, wl.d_qk, dtype=torch.float32, device=dev)
+    dkv = torch.empty(B, N, wl.d_qk, dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.workspace_size(dsa.OP_ATTN_BWD, B, T, N, wl.H, wl.d_v, wl.k),
+                     dtype=torch.uint8, device=dev)
+
+    def fn():
+        dsa.sparse_mla_attn_bwd(g["q"], g["kv"], idx, out, lse, dout, wl.sm_scale, dq=dq, dkv=dkv,
+                                workspace=ws)
+
+    for _ in range(2):
+        fn()
+    ms = timed(fn, steps, stream)
+    n_valid = int(((idx >= 0) & (idx < N)).sum().item())
+    rows = B * T
+    flop = 2.0 * (576 + 512 + 576 + 576 + 512) * wl.H * n_valid
+    nbytes = (rows * wl.H * (2 * wl.d_qk + 2 * 2 * wl.d_v + 4 + 4 * wl.d_qk) + n_valid * 2 * wl.d_qk
+              + B * N * 4 * wl.d_qk)
+    ach = flop / (ms / 1e3) / 1e12
+    return {"attn_bwd": {"ms": round(ms, 4), "rows": rows, "bound": "mfma", "achieved": round(ach, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop,
+                         "algorithmic_bytes": nbytes,
+                         "hbm_floor_ms": round(nbytes / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}}
+
+
 def cpu_baseline(wl, g, budget_s):
     """The CPU oracle on a bounded sample of the same workload: whole rows
     (index scores -> selection -> attention), timed on this host's cores."""
@@ -423,6 +461,9 @@ def main():
     # the indexer's alignment objective on this step's score rows (dense
     # warm-up form) and on its selected slots (sparse form)
     line["next"].update(time_indexer_kl(wl, scores, idx, args.steps, stream))
+    # the sparse attention backward on this step's selection
+    if wl.dtype == "bf16":
+        line["next"].update(time_attn_bwd(wl, g, idx, args.steps, stream))
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl, g, args.cpu_budget)

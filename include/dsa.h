@@ -72,7 +72,8 @@ typedef enum dsa_op {
     DSA_OP_TOPK = 0,
     DSA_OP_ATTN = 1,
     DSA_OP_FORWARD = 2,
-    DSA_OP_SELECT = 3
+    DSA_OP_SELECT = 3,
+    DSA_OP_ATTN_BWD = 4
 } dsa_op;
 
 /*
@@ -150,6 +151,44 @@ DSA_API dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int3
                                int B, int T, int N, int H, int d_qk, int d_v, int k,
                                float sm_scale, dsa_dtype attn_dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of dsa_sparse_mla_attn (bf16 MQA mode) for the sparse training
+ * stage ("Paper Breakdown: DeepSeek-V3.2", section 2, "Continued
+ * Pre-Training (§2.1.1)": the main model is trained through the sparse
+ * attention over the selected entries).  With z, P = softmax(z) and out as
+ * in dsa_sparse_mla_attn and dout the gradient of the loss w.r.t. out:
+ *     dP[h,i] = dout[b,t,h,:] . kv[b,idx[b,t,i],0:d_v]
+ *     dS[h,i] = sm_scale * P[h,i] * (dP[h,i] - dout[b,t,h,:] . out[b,t,h,:])
+ *     dq[b,t,h,:]         = sum_i dS[h,i] * kv[b,idx[b,t,i],:]
+ *     dkv[b,s,:]          = sum over (t,i) with idx[b,t,i] = s of
+ *                           sum_h dS[h,i] q[b,t,h,:]  (+ sum_h P[h,i] dout[b,t,h,:]
+ *                           on the first d_v columns)
+ * P is recomputed as exp(z - lse) from the forward's lse.
+ *
+ *  q, kv, idx  as passed to the forward (bf16; H = 128, d_qk = 576, d_v = 512)
+ *  out  [B,T,H,d_v] bf16  the forward's output
+ *  lse  [B,T,H]     f32   the forward's log-sum-exp (required)
+ *  dout [B,T,H,d_v] bf16
+ *  dq   [B,T,H,d_qk] f32  output, fully overwritten
+ *  dkv  [B,N,d_qk]   f32  output, fully overwritten (0 for rows no slot selects)
+ * Slots outside [0, N) contribute nothing; a token in several slots receives
+ * the sum.  Products run on bf16 MFMA with fp32 accumulation; P and dS are
+ * rounded to bf16 before the products that produce dq and dkv.  Each slot's
+ * latent-gradient vector (summed over the heads in fp32) is rounded to bf16,
+ * and the vectors of a token are summed in fp32 in an order that depends on
+ * scheduling, so the last bits of dkv vary from run to run.  Rows are
+ * processed 2048 at a time; the workspace (dsa_workspace_size(
+ * DSA_OP_ATTN_BWD, ...) bytes, 16-byte aligned, overwritten) holds one such
+ * block's P and dS tiles, slot vectors and per-token lists, plus a count and
+ * an offset per token of the batch (B*N of each).  attn_dtype must be DSA_BF16.
+ */
+DSA_API dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const int32_t* idx,
+                                   const void* out, const float* lse, const void* dout,
+                                   float* dq, float* dkv,
+                                   int B, int T, int N, int H, int d_qk, int d_v, int k,
+                                   float sm_scale, dsa_dtype attn_dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Index scores and top-k selection in one call: idx as dsa_topk_select would

@@ -27,13 +27,13 @@ import torch
 __all__ = [
     "DSAError", "lib", "lib_path", "indexer_scores", "topk_select", "sparse_mla_attn",
     "forward", "indexer_select", "cache_append", "indexer_kl", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD",
-    "OP_SELECT",
+    "OP_SELECT", "OP_ATTN_BWD", "sparse_mla_attn_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-OP_TOPK, OP_ATTN, OP_FORWARD, OP_SELECT = 0, 1, 2, 3
+OP_TOPK, OP_ATTN, OP_FORWARD, OP_SELECT, OP_ATTN_BWD = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.dsa_topk_select.restype = ci
     L.dsa_sparse_mla_attn.argtypes = [vp, vp, i32p, vp, fp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, sz, vp]
     L.dsa_sparse_mla_attn.restype = ci
+    L.dsa_sparse_mla_attn_bwd.argtypes = [vp, vp, i32p, vp, fp, vp, fp, fp, ci, ci, ci, ci, ci, ci, ci,
+                                          cf, ci, vp, sz, vp]
+    L.dsa_sparse_mla_attn_bwd.restype = ci
     L.dsa_forward.argtypes = [vp, fp, vp, fp, fp, vp, vp, vp, fp, i32p,
                               ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, sz, vp]
     L.dsa_forward.restype = ci
@@ -261,6 +264,41 @@ def sparse_mla_attn(q, kv, idx, d_v: int, sm_scale: float, out=None, lse: Option
                                        _stream(dev))
     _raise("dsa_sparse_mla_attn", st)
     return out, lse_t
+
+
+def sparse_mla_attn_bwd(q, kv, idx, out, lse, dout, sm_scale: float, dq=None, dkv=None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Gradients of sparse MQA attention (bf16).  Takes the forward's inputs,
+    its output and log-sum-exp and the output gradient; returns
+    (dq [B,T,H,d_qk] f32, dkv [B,N,d_qk] f32)."""
+    dt = _attn_dtype(q)
+    dev = q.device
+    B, T, H, d_qk = q.shape
+    N = kv.shape[1]
+    k = idx.shape[-1]
+    d_v = out.shape[-1]
+    _check("q", q, q.dtype, (B, T, H, d_qk), dev)
+    _check("kv", kv, q.dtype, (B, N, d_qk), dev)
+    _check("idx", idx, torch.int32, (B, T, k), dev)
+    _check("out", out, q.dtype, (B, T, H, d_v), dev)
+    _check("lse", lse, torch.float32, (B, T, H), dev)
+    _check("dout", dout, q.dtype, (B, T, H, d_v), dev)
+    if dq is None:
+        dq = torch.empty(B, T, H, d_qk, dtype=torch.float32, device=dev)
+    if dkv is None:
+        dkv = torch.empty(B, N, d_qk, dtype=torch.float32, device=dev)
+    _check("dq", dq, torch.float32, (B, T, H, d_qk), dev)
+    _check("dkv", dkv, torch.float32, (B, N, d_qk), dev)
+    need = workspace_size(OP_ATTN_BWD, B, T, N, H, d_v, k) if 1 <= k <= 2048 else 0
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = lib().dsa_sparse_mla_attn_bwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
+                                           _ptr(dout), _ptr(dq), _ptr(dkv), B, T, N, H, d_qk, d_v, k,
+                                           float(sm_scale), dt, _ptr(ws),
+                                           0 if ws is None else ws.numel() * ws.element_size(),
+                                           _stream(dev))
+    _raise("dsa_sparse_mla_attn_bwd", st)
+    return dq, dkv
 
 
 def forward(q_idx, k_idx, w, q, kv, *, k: int, q_offset: int, d_v: int, sm_scale: float,

@@ -131,7 +131,7 @@ dsa_status run_attn(const void* q, const void* kv, const int32_t* idx, void* out
 
 extern "C" {
 
-int dsa_version(void) { return (1 << 16) | 2; }
+int dsa_version(void) { return (1 << 16) | 3; }
 
 const char* dsa_status_string(dsa_status s) {
     switch (s) {
@@ -151,6 +151,7 @@ size_t dsa_workspace_size(int op, int B, int T, int N, int H, int d_v, int k) {
         case DSA_OP_TOPK: return topk_workspace_bytes(B, T, N, k);
         case DSA_OP_ATTN: return attn_ws(B, T, H, d_v, k);
         case DSA_OP_SELECT: return select_ws(B, T, N, k);
+        case DSA_OP_ATTN_BWD: return attn_bwd_workspace_bytes(B, T, N, k);
         case DSA_OP_FORWARD:
             return align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t)) +
                    attn_ws(B, T, H, d_v, k);
@@ -211,6 +212,22 @@ dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx
         return DSA_ERR_WORKSPACE;
     return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, workspace,
                     static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const int32_t* idx,
+                                   const void* out, const float* lse, const void* dout, float* dq,
+                                   float* dkv, int B, int T, int N, int H, int d_qk, int d_v, int k,
+                                   float sm_scale, dsa_dtype attn_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    dsa_status st = check_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype);
+    if (st != DSA_OK) return st;
+    if (!lse || !dout || !dq || !dkv) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dkv)) return DSA_ERR_INVALID_ARG;
+    if (attn_dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+    const size_t need = attn_bwd_workspace_bytes(B, T, N, k);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
+    return launch_attn_bwd_bf16(q, kv, idx, out, lse, dout, dq, dkv, B, T, N, k, sm_scale, workspace,
+                                static_cast<hipStream_t>(stream));
 }
 
 dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* k_idx,

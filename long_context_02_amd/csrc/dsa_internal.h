@@ -92,6 +92,17 @@ dsa_status launch_attn_f32(const float* q, const float* kv, const int32_t* idx, 
                            float* lse, int B, int T, int N, int H, int d_qk, int d_v, int k,
                            float sm_scale, hipStream_t stream);
 
+// ---- sparse attention backward (attention_bwd.hip) --------------------------
+// bf16 only (H = 128, d_qk = 576, d_v = 512).  dq [B,T,H,576] and dkv
+// [B,N,576] are fp32 and fully overwritten; the workspace holds one block of
+// rows' P and dS tiles, latent-gradient contribution rows and the per-token
+// lists, plus per-token counts and offsets.
+size_t attn_bwd_workspace_bytes(int B, int T, int N, int k);
+dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* idx, const void* out,
+                                const float* lse, const void* dout, float* dq, float* dkv, int B,
+                                int T, int N, int k, float sm_scale, void* workspace,
+                                hipStream_t stream);
+
 // ---- cache append (cache.hip) ---------------------------------------------
 // fp8: quantise the key rows (d_i = 128) into codes + scales; otherwise copy
 // f32 key rows.  Latent rows are copied as kv_row_bytes bytes.

@@ -116,6 +116,29 @@ def test_attention_rejects_bad_arguments():
     assert call(N=(1 << 31) // 1152 + 1) == 2             # bf16 rows beyond 32-bit offsets
 
 
+def test_attention_bwd_rejects_bad_arguments():
+    f = dsa.lib().dsa_sparse_mla_attn_bwd
+    need = dsa.workspace_size(dsa.OP_ATTN_BWD, 1, 4, 10, 128, 512, 64)
+    # P and dS tiles ([128 heads][32 slots] bf16 each) of every row
+    assert need >= 2 * 4 * 2 * 128 * 32 * 2
+    big = dsa.workspace_size(dsa.OP_ATTN_BWD, 1, 4096, 131072, 128, 512, 2048)
+    assert big >= 2 * 2048 * 64 * 128 * 32 * 2  # rows are processed 2048 at a time
+
+    def call(H=128, dqk=576, dv=512, k=64, scale=0.04, dt=dsa.BF16, lse=P, dout=P, dq=P, dkv=P,
+             ws=P, ws_bytes=None, N=10, T=4):
+        wb = need if ws_bytes is None else ws_bytes
+        return f(P, P, P, P, lse, dout, dq, dkv, 1, T, N, H, dqk, dv, k, scale, dt, ws, wb, None)
+
+    assert call(lse=None) == 1 and call(dout=None) == 1 and call(dq=None) == 1 and call(dkv=None) == 1
+    assert call(dq=ctypes.c_void_p(0x10004)) == 1          # misaligned
+    assert call(H=64) == 2 and call(dqk=512) == 2 and call(dv=256) == 2
+    assert call(k=0) == 1 and call(k=2049) == 2
+    assert call(scale=float("inf")) == 1
+    assert call(H=16, dqk=64, dv=64, dt=dsa.F32) == 2     # bf16 only
+    assert call(ws=None) == 3 and call(ws_bytes=need - 1) == 3
+    assert call(N=(1 << 31) // 1152 + 1) == 2
+
+
 def test_indexer_select_rejects_bad_arguments():
     f = dsa.lib().dsa_indexer_select
 
