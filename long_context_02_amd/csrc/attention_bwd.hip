@@ -88,6 +88,7 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
     __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + TK];
+    __shared__ __attribute__((aligned(16))) uint8_t sds[4 * 1024];  // dS fragments of the 4 waves
     __shared__ int s_last;
 
     // the two head halves of a row get ids 16j + x and 16j + 8 + x: the same
@@ -121,21 +122,16 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
     int rope_off[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) rope_off[a] = TK * LAT + m * ROPE + 16 * ((4 * a + g) ^ (m & 7));
-    const int tr_r = 4 * g + (m >> 2);
-    int tr_off[8];
-    {
-        const int sw = swz(tr_r), ch = (m & 3) >> 1;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            tr_off[j] = tr_r * LAT + 32 * (j ^ (sw >> 1)) + 16 * (ch ^ (sw & 1)) + 8 * (m & 1);
-    }
-    // transposed reads of the rope columns: 8 bytes of row tr_r at rope
-    // column 16*nr + 4*(m%4), i.e. chunk 2*nr + (m%4)/2, stored in slot
+    // transposed reads (rows tr_r and tr_r + 16): latent column block cb
+    // (< 32) is chunk 2*cb + (m%4)/2 of the row, in slot chunk ^ swz(row);
+    // rope column block nr is rope chunk 2*nr + (m%4)/2, in slot
     // chunk ^ (row % 8)
-    int trr_off[4];
-#pragma unroll
-    for (int nr = 0; nr < 4; ++nr)
-        trr_off[nr] = TK * LAT + tr_r * ROPE + 16 * ((2 * nr + ((m & 3) >> 1)) ^ (tr_r & 7)) + 8 * (m & 1);
+    const int tr_r = 4 * g + (m >> 2);
+    const int tr_sw = swz(tr_r);
+    const int tr_base = tr_r * LAT + 16 * (((m & 3) >> 1) ^ (tr_sw & 1)) + 8 * (m & 1);
+    const int tr_hi = tr_sw >> 1;
+    const int trr_base = TK * LAT + tr_r * ROPE + 8 * (m & 1);
+    const int trr_ch = (m & 3) >> 1, trr_sw = tr_r & 7;
 
     const i32x4 kv_rsrc = buffer_rsrc(kv_b, (unsigned)N * (unsigned)(2 * DQK));
     const int lane16 = lane << 4;
@@ -168,9 +164,14 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
     };
 
     bf16x8 qf[DQK / 32], dof[DV / 32];
-    f32x4 dqa[DQK / 16];
+    // dq of all 64 heads (4 blocks of 16) at this wave's 9 column blocks
+    // 9w..9w+8 (columns 144w..144w+143)
+    const int cb0 = 9 * wave_s;
+    f32x4 dqa[4][9];
 #pragma unroll
-    for (int i = 0; i < DQK / 16; ++i) dqa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int j = 0; j < 9; ++j) dqa[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float D = 0.f, lse2 = 0.f;
 
     auto compute = [&](const uint8_t* st, int tile, uint8_t* nxt) __attribute__((always_inline)) {
@@ -230,14 +231,21 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
                 uint2{pack_bf16(ds[4], ds[5]), pack_bf16(ds[6], ds[7])};
         }
 
-        // dq[head, col] += dS[head, key] C[key, col]; C^T fragments by
-        // transposed reads (keys 4g..4g+3 and 16+4g..16+4g+3 of column
-        // 16*cb + m), two blocks ahead of their MFMA
+        // dq[head, col] += dS[head, key] C[key, col].  The waves trade their
+        // dS fragments through LDS, so that each multiplies all 64 heads
+        // against its own nine column blocks: every C^T fragment (two
+        // transposed reads: keys 4g..4g+3 and 16+4g..16+4g+3 of column
+        // 16*cb + m) is read once per workgroup instead of once per wave.
+        *reinterpret_cast<bf16x8*>(sds + wave * 1024 + lane * 16) = dsa;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        bf16x8 da[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) da[hb] = *reinterpret_cast<const bf16x8*>(sds + hb * 1024 + lane * 16);
         auto cfrag = [&](int cb) __attribute__((always_inline)) -> bf16x8 {
-            int off;
-            if (cb < 32) off = tr_off[cb & 7] + 256 * (cb >> 3);
-            else off = trr_off[cb - 32];
-            const int step16 = cb < 32 ? 16 * LAT : 16 * ROPE;
+            const bool lat = cb < 32;
+            const int off = lat ? tr_base + 32 * ((cb & 7) ^ tr_hi) + 256 * (cb >> 3)
+                                : trr_base + 16 * ((2 * (cb - 32) + trr_ch) ^ trr_sw);
+            const int step16 = lat ? 16 * LAT : 16 * ROPE;
             const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + off));
             const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + off + step16));
             const uint4 vv = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1)),
@@ -247,13 +255,14 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
             return as_bf16x8(vv);
         };
         bf16x8 cf[3];
-        cf[0] = cfrag(0);
-        cf[1] = cfrag(1);
+        cf[0] = cfrag(cb0);
+        cf[1] = cfrag(cb0 + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cb = 0; cb < DQK / 16; ++cb) {
-            if (cb + 2 < DQK / 16) cf[(cb + 2) % 3] = cfrag(cb + 2);
-            dqa[cb] = mfma_bf16(dsa, cf[cb % 3], dqa[cb]);
+        for (int j = 0; j < 9; ++j) {
+            if (j + 2 < 9) cf[(j + 2) % 3] = cfrag(cb0 + j + 2);
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) dqa[hb][j] = mfma_bf16(da[hb], cf[j % 3], dqa[hb][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -301,12 +310,15 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
     }
     DSA_WAIT_VM(0);
 
-    // dq rows 4g + i of this wave's 16 heads, column 16*cb + m
-    float* dqw = dq + (row * H + hg * HG + 16 * wave + 4 * g) * DQK + m;
+    // dq rows 16*hb + 4g + i of the workgroup's 64 heads, column
+    // 16*(cb0 + j) + m
+    float* dqw = dq + (row * H + hg * HG + 4 * g) * DQK + 16 * cb0 + m;
 #pragma unroll
-    for (int cb = 0; cb < DQK / 16; ++cb)
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dqw[i * DQK + 16 * cb] = dqa[cb][i];
+        for (int j = 0; j < 9; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dqw[(16 * hb + i) * DQK + 16 * j] = dqa[hb][j][i];
 }
 
 // LDS row pitch of the staged Q and dO rows (16 bytes of padding keep the
