@@ -302,7 +302,8 @@ def time_attn_bwd(wl, g, idx, steps, stream):
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "algorithmic_flop": flop,
                          "algorithmic_bytes": nbytes,
-                         "hbm_floor_ms": round(nbytes / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}}
+                         "hbm_floor_ms": round(nbytes / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
+                         "traffic": measured_traffic("attn_bwd", wl)}}
 
 
 def cpu_baseline(wl, g, budget_s):
