@@ -62,7 +62,7 @@ void sparse_mla_attn_bf16(
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
-    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + TK];
+    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + 3 * TK];
     __shared__ int s_last;
     __shared__ int s_redo;
 
@@ -83,7 +83,7 @@ void sparse_mla_attn_bf16(
     __syncthreads();
     int my_last = -1;
     const int nslots_pad = (nslots + TK - 1) / TK * TK;
-    for (int i = tid; i < nslots_pad; i += NTA) {
+    for (int i = tid; i < nslots_pad + 3 * TK; i += NTA) {
         const int id = i < nslots ? idx[row * k + slot0 + i] : -1;
         sidx[i] = id;
         if (id >= 0 && id < N) my_last = i;
@@ -155,6 +155,8 @@ void sparse_mla_attn_bf16(
     const i32x4 kv_rsrc = buffer_rsrc(kv_b, (unsigned)N * (unsigned)(2 * DQK));
     const int lane16 = lane << 4;
     auto gather_id = [&](int tile) __attribute__((always_inline)) {
+        // (the lookahead reaches three tiles past the last one: sidx holds
+        // -1 there, and such tiles are never gathered)
         const int r = 8 * wave + (lane >> 3);
         int id = sidx[tile * TK + r];
         if (id < 0 || id >= N) id = dummy;
