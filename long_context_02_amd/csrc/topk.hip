@@ -87,24 +87,34 @@ __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores
     uint32_t* wkey = ckey + WREG * wave;
     int32_t* widx = cidx + WREG * wave;
     uint32_t fill = 0;  // wave-uniform
-    for (int base = 0; base < n_cand; base += 4 * TT) {
-        const int e = base + 64 * (16 * (lane >> 4) + wave) + 4 * (lane & 15);
-        float v[4];
-        load4(s, e, n_cand, vec, v);
+    // RU stretches per round: their loads are all in flight before the first
+    // is filtered (the row is read once, so the read rate is set by the
+    // bytes in flight per CU)
+    constexpr int RU = 4;
+    for (int base0 = 0; base0 < n_cand; base0 += 4 * TT * RU) {
+        float v[RU][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t key = fkey(v[j]);
-            const bool pass = e + j < n_cand && key >= theta;
-            const uint64_t bal = __ballot(pass);
-            const uint32_t c = (uint32_t)__popcll(bal);
-            if (c == 0u) continue;
-            const uint32_t pos = fill + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (pass && pos < (uint32_t)WREG) {
-                wkey[pos] = key;
-                widx[pos] = e + j;
+        for (int u = 0; u < RU; ++u)
+            load4(s, base0 + 4 * TT * u + 64 * (16 * (lane >> 4) + wave) + 4 * (lane & 15), n_cand, vec,
+                  v[u]);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int e = base0 + 4 * TT * u + 64 * (16 * (lane >> 4) + wave) + 4 * (lane & 15);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = fkey(v[u][j]);
+                const bool pass = e + j < n_cand && key >= theta;
+                const uint64_t bal = __ballot(pass);
+                const uint32_t c = (uint32_t)__popcll(bal);
+                if (c == 0u) continue;
+                const uint32_t pos = fill + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (pass && pos < (uint32_t)WREG) {
+                    wkey[pos] = key;
+                    widx[pos] = e + j;
+                }
+                fill += c;
             }
-            fill += c;
         }
     }
     // the wave's unused slots get key 0, below the (positive) threshold: never
