@@ -98,3 +98,31 @@ def test_bf16_large_logit_gap_reruns_exactly(T):
     print(f"  large-gap T={T}: lse spread {gap:.1f}", flush=True)
     check_attention(np64(out), ref_o, True, f"large gap T={T}")
     check_lse(np64(lse), ref_l, True, f"large gap T={T}")
+
+
+def test_bf16_largest_supported_context():
+    """N just under the 2^31 / 1152 rows that the gather's 32-bit byte
+    offsets cover: selections at the very end of the cache, and one row of
+    mixed low and high indices.  The oracle sees only the selected rows."""
+    dev = gpu_device()
+    N, H, dqk, dv, k = 1_864_000, 128, 576, 512, 2048
+    gen = torch.Generator(device=dev).manual_seed(31)
+    kv = torch.randn(1, N, dqk, generator=gen, device=dev, dtype=torch.bfloat16)
+    q = torch.randn(1, 2, H, dqk, generator=gen, device=dev, dtype=torch.bfloat16)
+    rng = np.random.default_rng(31)
+    idx = np.empty((1, 2, k), dtype=np.int32)
+    idx[0, 0] = np.arange(N - k, N)
+    idx[0, 1] = np.sort(np.concatenate([rng.choice(1000, 1000, replace=False),
+                                        N - 1 - rng.choice(200_000, k - 1000, replace=False)]))
+    scale = 1.0 / np.sqrt(dqk)
+    print("[attn] largest context", flush=True)
+    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx).to(dev), dv, scale)
+    torch.cuda.synchronize()
+    for t in range(2):
+        uniq, local = np.unique(idx[0, t], return_inverse=True)
+        rows = np64(kv[0, torch.from_numpy(uniq.astype(np.int64)).to(dev)])
+        o, l = oracle.sparse_mqa_attention_row(np64(q[0, t]), rows, local, dv, scale)
+        check_attention(np64(out[0, t]), o, True, f"largest context row {t}")
+        check_lse(np64(lse[0, t]), l, True, f"largest context row {t}")
+    del kv
+    torch.cuda.empty_cache()

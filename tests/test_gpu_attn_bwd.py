@@ -288,3 +288,49 @@ def test_full_size_sampled(name):
           f"rms dkv {rms_kv.check(name):.3g}", flush=True)
     del g, q, kv, out, lse, dq, dkv, dout
     torch.cuda.empty_cache()
+
+
+def test_bf16_largest_supported_context():
+    """N just under the 2^31 / 1152 rows the gather's 32-bit byte offsets
+    cover, selections at the end of the cache: dq of both rows and dkv of the
+    selected tokens against the oracle on the selected rows only, and
+    untouched rows exactly zero."""
+    dev = gpu_device()
+    N, H, dqk, dv, k = 1_864_000, 128, 576, 512, 2048
+    gen = torch.Generator(device=dev).manual_seed(32)
+    kv = torch.randn(1, N, dqk, generator=gen, device=dev, dtype=torch.bfloat16)
+    q = torch.randn(1, 2, H, dqk, generator=gen, device=dev, dtype=torch.bfloat16)
+    dout = torch.randn(1, 2, H, dv, generator=gen, device=dev, dtype=torch.bfloat16)
+    rng = np.random.default_rng(32)
+    idx = np.empty((1, 2, k), dtype=np.int32)
+    idx[0, 0] = np.arange(N - k, N)
+    idx[0, 1] = np.sort(np.concatenate([rng.choice(1000, 1000, replace=False),
+                                        N - 1 - rng.choice(5000, k - 1000, replace=False)]))
+    scale = 1.0 / np.sqrt(dqk)
+    idx_t = torch.from_numpy(idx).to(dev)
+    print("[attn_bwd] largest context", flush=True)
+    out, lse = dsa.sparse_mla_attn(q, kv, idx_t, dv, scale)
+    dq, dkv = dsa.sparse_mla_attn_bwd(q, kv, idx_t, out, lse, dout, scale)
+    torch.cuda.synchronize()
+    toks = np.unique(idx[0])
+    rows = np64(kv[0, torch.from_numpy(toks.astype(np.int64)).to(dev)])
+    ref = np.zeros((toks.size, dqk))
+    bound = np.zeros((toks.size, dqk))
+    mag = np.zeros((toks.size, dqk))
+    cnt = np.zeros(toks.size)
+    worst = 0.0
+    for t in range(2):
+        local = np.searchsorted(toks, idx[0, t])
+        r = _row_terms(np64(q[0, t]), rows, local, np64(dout[0, t]), dv, scale)
+        worst = max(worst, _check("dq", np64(dq[0, t]), r["dq"], r["dq_bound"], f"largest context row {t}"))
+        ref[r["uniq"]] += r["dkv_sub"]
+        np.add.at(bound, r["sel"], r["dc_bound"])
+        np.add.at(mag, r["sel"], r["dc_mag"])
+        np.add.at(cnt, r["sel"], 1)
+    got = np64(dkv[0, torch.from_numpy(toks.astype(np.int64)).to(dev)])
+    worst = max(worst, _check("dkv", got, ref, bound + cnt[:, None] * 2.0 ** -24 * mag, "largest context"))
+    # rows between the two selected ranges are untouched
+    assert not np64(dkv[0, 5000:6000]).any() and not np64(dkv[0, N - 300_000:N - 299_000]).any()
+    print(f"[attn_bwd] largest context: worst err/bound {worst:.3g}", flush=True)
+    del kv, dkv
+    torch.cuda.empty_cache()
