@@ -100,7 +100,8 @@ def check_scores(gpu, ref, s_abs, coeff, where=""):
     assert np.array_equal(ninf_g, ninf_r), f"{where}: -inf pattern differs"
     fin = ~ninf_r
     tol = coeff * s_abs + 2.0 ** -20 * np.abs(np.where(fin, ref, 0))
-    err = np.abs(np.where(fin, gpu - ref, 0))
+    err = np.zeros_like(ref)
+    err[fin] = np.abs(gpu[fin] - ref[fin])
     bad = err > np.where(fin, tol, 0)
     assert not bad.any(), (f"{where}: {bad.sum()} scores off; worst err {err.max():.3e}")
     return float((err / np.maximum(np.where(fin, s_abs, 1), 1e-300)).max())

@@ -31,8 +31,9 @@ def _stats(I, p):
     with np.errstate(divide="ignore"):
         lp = np.where(p > 0, np.abs(np.log(np.where(p > 0, p, 1.0))), 0.0)
     fin = np.isfinite(d)
-    tol_l = P * (2.0 ** -16 + abs(lse) * 2.0 ** -22) + 2.0 ** -16 * np.sum(p * lp + np.where(fin, p * np.abs(d), 0))
-    tol_g = P * q * (2.0 ** -16 + (abs(lse) + np.where(fin, np.abs(d), 0)) * 2.0 ** -21) + 2.0 ** -22 * (P * q + p)
+    ad = np.where(fin, np.abs(np.where(fin, d, 0.0)), 0.0)  # |I - lse|, 0 at masked (-inf) entries
+    tol_l = P * (2.0 ** -16 + abs(lse) * 2.0 ** -22) + 2.0 ** -16 * np.sum(p * lp + p * ad)
+    tol_g = P * q * (2.0 ** -16 + (abs(lse) + ad) * 2.0 ** -21) + 2.0 ** -22 * (P * q + p)
     return tol_l, tol_g
 
 
