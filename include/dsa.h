@@ -27,6 +27,16 @@
  *    is never validated (NaN inputs do not fault; see each call).
  *  - Stateless and re-entrant: concurrent calls on different streams with
  *    disjoint outputs and workspaces are safe.
+ *  - Debug validation: when the environment variable DSA_VALIDATE is "1" at
+ *    the time of the call, the entry points that take token indices or cache
+ *    positions from the caller (dsa_sparse_mla_attn, dsa_sparse_mla_attn_bwd,
+ *    dsa_indexer_kl with idx, dsa_cache_append) first check them on the
+ *    stream: an index that is neither -1 nor inside [0, N), or a cache row
+ *    pos[b] + t outside [0, N), makes the call return DSA_ERR_BAD_INDEX
+ *    without launching anything else.  Such calls wait for the stream (the
+ *    only calls that do), and validated calls that overlap on one device
+ *    share the library's single device counter.  Without it, such entries
+ *    are skipped as each call describes.
  *
  * Supported shapes
  *  - indexer: (H_I, d_I, idx_dtype) = (8, 128, DSA_FP8_E4M3FN) or

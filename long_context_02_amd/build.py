@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_bwd.hip", "cache.hip", "kl.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_bwd.hip", "cache.hip", "kl.hip", "validate.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

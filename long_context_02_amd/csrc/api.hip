@@ -210,8 +210,12 @@ dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx
     const size_t need = attn_workspace_bytes(B, T, H, d_v, k, attn_dtype);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return DSA_ERR_WORKSPACE;
-    return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, workspace,
-                    static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validation_enabled()) {
+        st = validate_indices(idx, (size_t)B * T * k, N, s);
+        if (st != DSA_OK) return st;
+    }
+    return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, workspace, s);
 }
 
 dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const int32_t* idx,
@@ -226,8 +230,12 @@ dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const int32_t*
     if (attn_dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
     const size_t need = attn_bwd_workspace_bytes(B, T, N, k);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
-    return launch_attn_bwd_bf16(q, kv, idx, out, lse, dout, dq, dkv, B, T, N, k, sm_scale, workspace,
-                                static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validation_enabled()) {
+        st = validate_indices(idx, (size_t)B * T * k, N, s);
+        if (st != DSA_OK) return st;
+    }
+    return launch_attn_bwd_bf16(q, kv, idx, out, lse, dout, dq, dkv, B, T, N, k, sm_scale, workspace, s);
 }
 
 dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* k_idx,
@@ -293,8 +301,13 @@ dsa_status dsa_cache_append(const float* k_new, const void* kv_new, void* k_cach
     } else {
         return attn_dtype == DSA_FP8_E4M3FN ? DSA_ERR_UNSUPPORTED : DSA_ERR_INVALID_ARG;
     }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validation_enabled()) {
+        const dsa_status st = validate_positions(pos, B, T, N, s);
+        if (st != DSA_OK) return st;
+    }
     return launch_cache_append(k_new, kv_new, k_cache, k_cache_scale, kv_cache, pos, B, T, N, d_I,
-                               row_bytes, fp8, static_cast<hipStream_t>(stream));
+                               row_bytes, fp8, s);
 }
 
 dsa_status dsa_indexer_kl(const float* scores, const float* p, const int32_t* idx, float* loss,
@@ -312,8 +325,12 @@ dsa_status dsa_indexer_kl(const float* scores, const float* p, const int32_t* id
     } else {
         if (q_offset < 0 || (long long)q_offset + T > N) return DSA_ERR_INVALID_ARG;
     }
-    return launch_indexer_kl(scores, p, idx, loss, grad, B, T, N, k, q_offset,
-                             static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (idx && validation_enabled()) {
+        const dsa_status st = validate_indices(idx, (size_t)B * T * k, N, s);
+        if (st != DSA_OK) return st;
+    }
+    return launch_indexer_kl(scores, p, idx, loss, grad, B, T, N, k, q_offset, s);
 }
 
 }  // extern "C"

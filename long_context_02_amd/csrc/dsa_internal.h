@@ -117,6 +117,14 @@ dsa_status launch_cache_append(const float* k_new, const void* kv_new, void* k_c
 dsa_status launch_indexer_kl(const float* scores, const float* p, const int32_t* idx, float* loss,
                              float* grad, int B, int T, int N, int k, int q_offset, hipStream_t stream);
 
+// ---- debug validation of caller indices (validate.hip) -----------------------
+// validation_enabled(): the environment holds DSA_VALIDATE=1 (read per call).
+// The validators count bad entries on stream s, wait for it and return
+// DSA_ERR_BAD_INDEX if there are any.
+bool validation_enabled();
+dsa_status validate_indices(const int32_t* idx, size_t n, int N, hipStream_t s);
+dsa_status validate_positions(const int32_t* pos, int B, int T, int N, hipStream_t s);
+
 inline dsa_status launch_status() {
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
