@@ -83,16 +83,38 @@ void sparse_mla_attn_bf16(
     __syncthreads();
     int my_last = -1;
     const int nslots_pad = (nslots + TK - 1) / TK * TK;
-    for (int i = tid; i < nslots_pad + 3 * TK; i += NTA) {
-        const int id = i < nslots ? idx[row * k + slot0 + i] : -1;
-        sidx[i] = id;
-        if (id >= 0 && id < N) my_last = i;
+    // this wave's 32 query heads (two blocks of 16) as B operands
+    bf16x8 qf[2][DQK / 32];
+    {
+        // all of a thread's index loads are issued before the first is
+        // waited for (a loop that stores each index as it arrives waits for
+        // one memory round trip per iteration), and Q's loads right behind
+        // them, so that Q arrives while the indices are used
+        constexpr int PER = (SLOTS + 3 * TK + NTA - 1) / NTA;
+        int id[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * NTA;
+            id[j] = i < nslots ? idx[row * k + slot0 + i] : -1;
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const uint16_t* qh = q + (row * H + 32 * wave + 16 * hb + m) * DQK + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < DQK / 32; ++ks)
+                qf[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * NTA;
+            if (i < nslots_pad + 3 * TK) {
+                sidx[i] = id[j];
+                if (id[j] >= 0 && id[j] < N) my_last = i;
+            }
+        }
     }
     if (my_last >= 0) atomicMax(&s_last, my_last);
 
-    // this wave's 32 query heads (two blocks of 16) as B operands; loaded
-    // once the first gather loads are in flight
-    bf16x8 qf[2][DQK / 32];
     __syncthreads();
     const int last = s_last;
     const int n_tiles = (last + TK) / TK;  // 0 when no slot is valid
@@ -297,21 +319,14 @@ void sparse_mla_attn_bf16(
         compute(cur, it, nxt);
     };
 
-    // the first pass's ring prologue, then Q (k = 8*(l/16)+j within each
-    // 32-wide step of d) while those loads are in flight
+    // the first pass's ring prologue; then all of Q (k = 8*(l/16)+j within
+    // each 32-wide step of d, loaded with the slot indices) is in registers
+    // before the loop: the waits the compiler would otherwise place at Q's
+    // first uses inside the loop would also wait for the gather loads it
+    // does not know about
     issue(st0, 0);
     issue(st1, 1);
     issue(st2, 2);
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const uint16_t* qh = q + (row * H + 32 * wave + 16 * hb + m) * DQK + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < DQK / 32; ++ks)
-            qf[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
-    }
-    // all of Q is in registers before the loop: the waits the compiler would
-    // otherwise place at Q's first uses inside the loop would also wait for
-    // the gather loads it does not know about
     DSA_WAIT_VM(0);
 
     for (int pass = 0; pass < 2; ++pass) {

@@ -66,10 +66,21 @@ __device__ __forceinline__ int load_slots(const int32_t* __restrict__ idx_row, i
     __syncthreads();
     int my_last = -1;
     const int k_pad = (k + TK - 1) / TK * TK;
-    for (int i = tid; i < k_pad; i += NT) {
-        const int id = i < k ? idx_row[i] : -1;
-        sidx[i] = id;
-        if (id >= 0 && id < N) my_last = i;
+    // every load is issued before the first is waited for
+    constexpr int PER = (SLOTS + NT - 1) / NT;
+    int id[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * NT;
+        id[j] = i < k ? idx_row[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * NT;
+        if (i < k_pad) {
+            sidx[i] = id[j];
+            if (id[j] >= 0 && id[j] < N) my_last = i;
+        }
     }
     if (my_last >= 0) atomicMax(s_last, my_last);
     __syncthreads();

@@ -223,7 +223,14 @@ __global__ __launch_bounds__(STT) void topk_seg_collect(const float* __restrict_
                                         e + 2 < s1 ? fkey(v[2]) : 0u, e + 3 < s1 ? fkey(v[3]) : 0u);
         if (e >= s1) kst[tid + STT * i].x = 0u;
     }
-    for (int i = tid; i < BINS; i += STT) hist[i] = w[WS_HIST + i];
+    {
+        constexpr int HPT = BINS / STT;
+        uint32_t hv[HPT];
+#pragma unroll
+        for (int j = 0; j < HPT; ++j) hv[j] = w[WS_HIST + tid + j * STT];
+#pragma unroll
+        for (int j = 0; j < HPT; ++j) hist[tid + j * STT] = hv[j];
+    }
     __syncthreads();
     find_bin(hist, BINS, (uint32_t)k, sh, res);
     const uint32_t b1 = res[0], eq1 = res[2];
@@ -275,6 +282,31 @@ __global__ __launch_bounds__(STT) void topk_seg_collect(const float* __restrict_
     }
 }
 
+// A row's candidate list (n_c <= CAPG keys and token indices) from its
+// workspace into LDS; every load is issued before the first is waited for
+// (a loop that stores each entry as it arrives waits for one memory round
+// trip per iteration).
+__device__ __forceinline__ void load_candidates(const uint32_t* __restrict__ wr, int n_c, uint32_t* ckey,
+                                                int32_t* cidx) {
+    constexpr int PER = (CAPG + TT - 1) / TT;
+    const int tid = threadIdx.x;
+    uint32_t kr[PER], ir[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * TT;
+        kr[j] = i < n_c ? wr[WS_CKEY + i] : 0u;
+        ir[j] = i < n_c ? wr[WS_CIDX + i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * TT;
+        if (i < n_c) {
+            ckey[i] = kr[j];
+            cidx[i] = (int32_t)ir[j];
+        }
+    }
+}
+
 constexpr int FIN_LDS_WORDS = 2 * CAPG + BINS + NW + 1 + 3;
 constexpr int K3_LDS_WORDS = FIN_LDS_WORDS > ROW_LDS_WORDS ? FIN_LDS_WORDS : ROW_LDS_WORDS;
 
@@ -303,10 +335,7 @@ __global__ __launch_bounds__(TT) void topk_seg_finalize(const float* __restrict_
     uint32_t* res = sh + NW + 1;                              // 3
     const int n_def = (int)w[WS_CTR + 0], n_c = (int)w[WS_CTR + 1];
     const int32_t* gdef = reinterpret_cast<const int32_t*>(w + WS_DEF);
-    for (int i = tid; i < n_c; i += TT) {
-        ckey[i] = w[WS_CKEY + i];
-        cidx[i] = reinterpret_cast<const int32_t*>(w + WS_CIDX)[i];
-    }
+    load_candidates(w, n_c, ckey, cidx);
     const uint32_t r1 = (uint32_t)(k - n_def);  // picks still to make among the candidates
     // digits 2 and 3 (key bits 19..10 and 9..0) give the exact k-th key
     for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
@@ -399,10 +428,7 @@ __global__ __launch_bounds__(TT) void topk_cand_select(
     uint32_t* hist = reinterpret_cast<uint32_t*>(cidx + CAPG);   // BINS, later the bitmap
     uint32_t* sh = hist + BINS;                                  // NW + 1
     uint32_t* res = sh + NW + 1;                                 // 3
-    for (int i = tid; i < n_c; i += TT) {
-        ckey[i] = wr[WS_CKEY + i];
-        cidx[i] = (int32_t)wr[WS_CIDX + i];
-    }
+    load_candidates(wr, n_c, ckey, cidx);
     __syncthreads();
     select_candidates(ckey, cidx, n_c, k, n_cand, out, hist, sh, res);
 }
