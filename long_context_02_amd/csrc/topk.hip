@@ -134,7 +134,7 @@ __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores
         select_row(s, out, n_cand, k, carve_row_lds(lds));
         return;
     }
-    select_candidates(ckey, cidx, CAP1, k, n_cand, out, hist, sh, res);
+    select_candidates<TT, true>(ckey, cidx, CAP1, k, n_cand, out, hist, sh, res);
 }
 
 // ---------------------------------------------------------------------------

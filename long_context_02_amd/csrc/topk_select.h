@@ -386,7 +386,10 @@ __device__ void emit_ascending(const int32_t* __restrict__ sure, int n_sure, con
 // order) written to out in ascending index order: the k-th key by three radix
 // digits (12, 10, 10 bits), the lowest-index ties, bitmap emission over
 // [0, n_cand).  hist: BINS words of LDS; sh: NTH/64 + 1 words; res: 3.
-template <int NTH = TT>
+// PADDED: the list also holds unused slots of key 0 below every candidate
+// (the one-pass row selection); they are left out of the first histogram,
+// where they would all hit one bin, and change no count above that bin.
+template <int NTH = TT, bool PADDED = false>
 __device__ __forceinline__ void select_candidates(const uint32_t* ckey, const int32_t* cidx, int n_c, int k,
                                   int n_cand, int32_t* __restrict__ out, uint32_t* hist,
                                   uint32_t* sh, uint32_t* res) {
@@ -394,7 +397,8 @@ __device__ __forceinline__ void select_candidates(const uint32_t* ckey, const in
     for (int i = tid; i < BINS; i += NTH) hist[i] = 0u;
     __syncthreads();
     #pragma unroll 1
-    for (int i = tid; i < n_c; i += NTH) atomicAdd(&hist[ckey[i] >> 20], 1u);
+    for (int i = tid; i < n_c; i += NTH)
+        if (!PADDED || ckey[i] != 0u) atomicAdd(&hist[ckey[i] >> 20], 1u);
     __syncthreads();
     find_bin<NTH>(hist, BINS, (uint32_t)k, sh, res);
     const uint32_t b1 = res[0], r1 = (uint32_t)k - res[1];
