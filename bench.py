@@ -282,7 +282,7 @@ def time_attn_bwd(wl, g, idx, steps, stream):
     dout = torch.randn(out.shape, generator=gen, device=dev, dtype=out.dtype)
     dq = torch.empty(B, T, wl.H, wl.d_qk, dtype=torch.float32, device=dev)
     dkv = torch.empty(B, N, wl.d_qk, dtype=torch.float32, device=dev)
-    ws = torch.empty(dsa.workspace_size(dsa.OP_ATTN_BWD, B, T, N, wl.H, wl.d_v, wl.k),
+    ws = torch.empty(dsa.workspace_size(dsa.OP_ATTN_BWD, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k),
                      dtype=torch.uint8, device=dev)
 
     def fn():
@@ -378,7 +378,7 @@ def main():
     g = make_inputs(wl, seed=0, device=dev)
     B, T, N = wl.B, wl.T, wl.N
     out = torch.empty(B, T, wl.H, wl.d_v, dtype=g["q"].dtype, device=dev)
-    ws = torch.empty(dsa.workspace_size(dsa.OP_FORWARD, B, T, N, wl.H, wl.d_v, wl.k),
+    ws = torch.empty(dsa.workspace_size(dsa.OP_FORWARD, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -400,11 +400,11 @@ def main():
     # score and top-k kernels the same way
     scores = torch.empty(B, T, N, dtype=torch.float32, device=dev)
     idx = torch.empty(B, T, wl.k, dtype=torch.int32, device=dev)
-    attn_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_ATTN, B, T, N, wl.H, wl.d_v, wl.k)),
+    attn_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_ATTN, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k)),
                           dtype=torch.uint8, device=dev)
-    sel_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_SELECT, B, T, N, 1, 1, wl.k)),
+    sel_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_SELECT, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k)),
                          dtype=torch.uint8, device=dev)
-    topk_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_TOPK, B, T, N, 1, 1, wl.k)),
+    topk_ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_TOPK, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k)),
                           dtype=torch.uint8, device=dev)
     step_parts = {
         "select": lambda: dsa.indexer_select(g["q_idx"], g["k_idx"], g["w"], wl.k, wl.q_offset,

@@ -225,12 +225,18 @@ DSA_API dsa_status dsa_indexer_select(const void* q_idx, const float* q_idx_scal
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The whole DSA path: indexer scores -> top-k selection -> sparse attention,
- * for prefill, decode and chunked prefill alike (see q_offset above).
+ * The whole DSA path ("Paper Breakdown: DeepSeek-V3.2", section 2
+ * "Architecture: DSA (§2.1)": the lightning indexer scores every earlier
+ * token, the fine-grained selector keeps the tokens in Top-k(I[t,:]), and
+ * attention runs over their latent entries, under "DSA under MLA (MQA
+ * Mode)"): indexer scores -> top-k selection -> sparse attention, for
+ * prefill, decode and chunked prefill alike (see q_offset above).
  * Arguments are those of the calls above; idx_out [B,T,k] receives the
  * selected indices when non-NULL.  The selection is dsa_indexer_select's.
  * The workspace holds the score matrix and the other intermediates: size it
- * with dsa_workspace_size(DSA_OP_FORWARD).
+ * with dsa_workspace_size(DSA_OP_FORWARD, B, T, N, H_I, H, d_v, k).
+ * Errors as for the calls above; nothing is launched when an argument check
+ * fails.
  */
 DSA_API dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale,
                        const void* k_idx, const float* k_idx_scale,
@@ -297,9 +303,14 @@ DSA_API dsa_status dsa_indexer_kl(const float* scores, const float* p, const int
 
 /*
  * Workspace bytes needed by op (a dsa_op) for these sizes; 0 means none.
- * Returns (size_t)-1 for arguments that no call would accept.
+ * The sizes are those passed to the call the workspace is for: B, T, N as
+ * above, H_I indexer heads (DSA_OP_SELECT, DSA_OP_FORWARD), H query heads
+ * and d_v value width (DSA_OP_ATTN, DSA_OP_ATTN_BWD, DSA_OP_FORWARD), k
+ * selected tokens per query; an op ignores the sizes it does not use, but
+ * each must be >= 1.  Returns (size_t)-1 for arguments that no call would
+ * accept (an unknown op, a size below 1, k above 2048).
  */
-DSA_API size_t dsa_workspace_size(int op, int B, int T, int N, int H, int d_v, int k);
+DSA_API size_t dsa_workspace_size(int op, int B, int T, int N, int H_I, int H, int d_v, int k);
 
 /* Static, NUL-terminated description of a status code. */
 DSA_API const char* dsa_status_string(dsa_status s);

@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_cache_append.restype = ci
     L.dsa_indexer_kl.argtypes = [fp, fp, i32p, fp, fp, ci, ci, ci, ci, ci, vp]
     L.dsa_indexer_kl.restype = ci
-    L.dsa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    L.dsa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     L.dsa_workspace_size.restype = sz
     L.dsa_status_string.argtypes = [ci]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -142,8 +142,8 @@ def _raise(fn, st):
         raise DSAError(fn, st)
 
 
-def workspace_size(op: int, B: int, T: int, N: int, H: int, d_v: int, k: int) -> int:
-    n = lib().dsa_workspace_size(op, B, T, N, H, d_v, k)
+def workspace_size(op: int, B: int, T: int, N: int, H_I: int, H: int, d_v: int, k: int) -> int:
+    n = lib().dsa_workspace_size(op, B, T, N, H_I, H, d_v, k)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("dsa_workspace_size: invalid arguments")
     return n
@@ -207,7 +207,7 @@ def indexer_select(q_idx, k_idx, w, k: int, q_offset: int, q_idx_scale=None, k_i
     if out is None:
         out = torch.empty(B, T, k, dtype=torch.int32, device=dev)
     _check("out", out, torch.int32, (B, T, k), dev)
-    need = workspace_size(OP_SELECT, B, T, N, 1, 1, k) if 1 <= k <= 2048 else 0
+    need = workspace_size(OP_SELECT, B, T, N, H_I, 1, 1, k) if 1 <= k <= 2048 else 0
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
         st = lib().dsa_indexer_select(_ptr(q_idx), _ptr(q_idx_scale), _ptr(k_idx), _ptr(k_idx_scale),
@@ -226,7 +226,7 @@ def topk_select(scores: torch.Tensor, k: int, q_offset: int, out: Optional[torch
     if out is None:
         out = torch.empty(B, T, k, dtype=torch.int32, device=dev)
     _check("out", out, torch.int32, (B, T, k), dev)
-    need = workspace_size(OP_TOPK, B, T, N, 1, 1, k) if 1 <= k <= 2048 else 0
+    need = workspace_size(OP_TOPK, B, T, N, 1, 1, 1, k) if 1 <= k <= 2048 else 0
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
         st = lib().dsa_topk_select(_ptr(scores), _ptr(out), B, T, N, k, q_offset, _ptr(ws),
@@ -255,7 +255,7 @@ def sparse_mla_attn(q, kv, idx, d_v: int, sm_scale: float, out=None, lse: Option
         _check("lse", lse_t, torch.float32, (B, T, H), dev)
     elif lse:
         lse_t = torch.empty(B, T, H, dtype=torch.float32, device=dev)
-    need = workspace_size(OP_ATTN, B, T, N, H, d_v, k) if 1 <= k <= 2048 else 0
+    need = workspace_size(OP_ATTN, B, T, N, 1, H, d_v, k) if 1 <= k <= 2048 else 0
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
         st = lib().dsa_sparse_mla_attn(_ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse_t),
@@ -289,7 +289,7 @@ def sparse_mla_attn_bwd(q, kv, idx, out, lse, dout, sm_scale: float, dq=None, dk
         dkv = torch.empty(B, N, d_qk, dtype=torch.float32, device=dev)
     _check("dq", dq, torch.float32, (B, T, H, d_qk), dev)
     _check("dkv", dkv, torch.float32, (B, N, d_qk), dev)
-    need = workspace_size(OP_ATTN_BWD, B, T, N, H, d_v, k) if 1 <= k <= 2048 else 0
+    need = workspace_size(OP_ATTN_BWD, B, T, N, 1, H, d_v, k) if 1 <= k <= 2048 else 0
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
         st = lib().dsa_sparse_mla_attn_bwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
@@ -323,7 +323,7 @@ def forward(q_idx, k_idx, w, q, kv, *, k: int, q_offset: int, d_v: int, sm_scale
         torch.empty(B, T, k, dtype=torch.int32, device=dev) if idx_out else None)
     if idx_t is not None:
         _check("idx_out", idx_t, torch.int32, (B, T, k), dev)
-    need = workspace_size(OP_FORWARD, B, T, N, H, d_v, k)
+    need = workspace_size(OP_FORWARD, B, T, N, H_I, H, d_v, k)
     ws = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
         st = lib().dsa_forward(_ptr(q_idx), _ptr(q_idx_scale), _ptr(k_idx), _ptr(k_idx_scale), _ptr(w),

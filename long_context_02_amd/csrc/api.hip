@@ -145,8 +145,9 @@ const char* dsa_status_string(dsa_status s) {
     return "unknown dsa_status";
 }
 
-size_t dsa_workspace_size(int op, int B, int T, int N, int H, int d_v, int k) {
-    if (B < 1 || T < 1 || N < 1 || k < 1 || k > kMaxK || H < 1 || d_v < 1) return (size_t)-1;
+size_t dsa_workspace_size(int op, int B, int T, int N, int H_I, int H, int d_v, int k) {
+    if (B < 1 || T < 1 || N < 1 || k < 1 || k > kMaxK || H_I < 1 || H < 1 || d_v < 1)
+        return (size_t)-1;
     switch (op) {
         case DSA_OP_TOPK: return topk_workspace_bytes(B, T, N, k);
         case DSA_OP_ATTN: return attn_ws(B, T, H, d_v, k);
@@ -178,7 +179,8 @@ dsa_status dsa_topk_select(const float* scores, int32_t* idx, int B, int T, int 
     if (k < 1) return DSA_ERR_INVALID_ARG;
     if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
     const size_t need = topk_workspace_bytes(B, T, N, k);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return DSA_ERR_WORKSPACE;
     return launch_topk(scores, idx, B, T, N, k, q_offset, workspace,
                        static_cast<hipStream_t>(stream));
 }
@@ -253,7 +255,7 @@ dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* 
                     sm_scale, attn_dtype);
     if (st != DSA_OK) return st;
     if (idx_out && !aligned16(idx_out)) return DSA_ERR_INVALID_ARG;
-    const size_t need = dsa_workspace_size(DSA_OP_FORWARD, B, T, N, H, d_v, k);
+    const size_t need = dsa_workspace_size(DSA_OP_FORWARD, B, T, N, H_I, H, d_v, k);
     if (need == (size_t)-1) return DSA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
 

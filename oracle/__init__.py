@@ -41,7 +41,6 @@ from .dsa import (  # noqa: F401
     sparse_mqa_attention_bwd,
     sparse_mqa_attention_bwd_row,
     dsa_forward,
-    default_sm_scale,
     cache_append,
     indexer_kl,
     indexer_kl_dense_row,

@@ -309,11 +309,6 @@ def dsa_forward(q_idx, k_idx, w, q, kv, *, k, q_offset, d_v, sm_scale,
     return {"scores": scores, "idx": idx, "out": out, "lse": lse, "rows": rows}
 
 
-def default_sm_scale(d_qk: int) -> float:
-    """Softmax scale 1/sqrt(d_qk) (the rule the small fp32 workload states)."""
-    return 1.0 / math.sqrt(d_qk)
-
-
 # --------------------------------------------------------------------------
 # Cache append (the step before the path at decode)
 # --------------------------------------------------------------------------

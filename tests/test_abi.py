@@ -41,27 +41,43 @@ def test_status_strings_and_version():
 def test_workspace_sizes():
     # top-k needs none for long batches; batches of at most 255 rows hold
     # a per-row histogram, counters and candidate lists
-    assert dsa.workspace_size(dsa.OP_TOPK, 1, 8192, 8192, 128, 512, 2048) == 0
-    seg = dsa.workspace_size(dsa.OP_TOPK, 64, 1, 131072, 128, 512, 2048)
+    assert dsa.workspace_size(dsa.OP_TOPK, 1, 8192, 8192, 8, 128, 512, 2048) == 0
+    seg = dsa.workspace_size(dsa.OP_TOPK, 64, 1, 131072, 8, 128, 512, 2048)
     assert seg >= 64 * (4096 + 2048 + 2 * 12288) * 4
     # forward holds the fp32 score matrix and the indices
-    fwd = dsa.workspace_size(dsa.OP_FORWARD, 1, 4096, 131072, 128, 512, 2048)
+    fwd = dsa.workspace_size(dsa.OP_FORWARD, 1, 4096, 131072, 8, 128, 512, 2048)
     assert fwd >= 4096 * 131072 * 4 + 4096 * 2048 * 4
     # decode splits the 2048 slots of its 64 rows over 4 workgroups each:
     # bf16 O rows plus fp32 (max, sum) per split and head
-    att = dsa.workspace_size(dsa.OP_ATTN, 64, 1, 131072, 128, 512, 2048)
+    att = dsa.workspace_size(dsa.OP_ATTN, 64, 1, 131072, 8, 128, 512, 2048)
     assert att >= 64 * 4 * 128 * (512 * 2 + 2 * 4)
     # prefill-sized batches need no split workspace; f32 shapes never do
-    assert dsa.workspace_size(dsa.OP_ATTN, 1, 8192, 8192, 128, 512, 2048) == 0
-    assert dsa.workspace_size(dsa.OP_ATTN, 1, 4, 256, 16, 64, 64) == 0
+    assert dsa.workspace_size(dsa.OP_ATTN, 1, 8192, 8192, 8, 128, 512, 2048) == 0
+    assert dsa.workspace_size(dsa.OP_ATTN, 1, 4, 256, 8, 16, 64, 64) == 0
     # the fused selection holds the scores and, for few rows, the row lists
-    sel = dsa.workspace_size(dsa.OP_SELECT, 64, 1, 131072, 1, 1, 2048)
+    sel = dsa.workspace_size(dsa.OP_SELECT, 64, 1, 131072, 8, 1, 1, 2048)
     assert sel >= 64 * 131072 * 4 + seg
-    assert dsa.workspace_size(dsa.OP_SELECT, 1, 4096, 131072, 1, 1, 2048) >= 4096 * 131072 * 4
+    assert dsa.workspace_size(dsa.OP_SELECT, 1, 4096, 131072, 8, 1, 1, 2048) >= 4096 * 131072 * 4
     with pytest.raises(ValueError):
-        dsa.workspace_size(dsa.OP_FORWARD, 1, 1, 1, 128, 512, 4096)
+        dsa.workspace_size(dsa.OP_FORWARD, 1, 1, 1, 8, 128, 512, 4096)
     with pytest.raises(ValueError):
-        dsa.workspace_size(7, 1, 1, 1, 1, 1, 1)
+        dsa.workspace_size(7, 1, 1, 1, 8, 1, 1, 1)
+    with pytest.raises(ValueError):  # indexer heads must be >= 1
+        dsa.workspace_size(dsa.OP_SELECT, 64, 1, 131072, 0, 128, 512, 2048)
+
+
+def test_workspace_size_takes_eight_sizes():
+    # the C signature is (op, B, T, N, H_I, H, d_v, k): called directly
+    # through ctypes with explicit argument types
+    L = ctypes.CDLL(dsa.lib_path())
+    f = L.dsa_workspace_size
+    f.argtypes = [ctypes.c_int] * 8
+    f.restype = ctypes.c_size_t
+    fwd = f(dsa.OP_FORWARD, 64, 1, 131072, 8, 128, 512, 2048)
+    assert fwd == dsa.workspace_size(dsa.OP_FORWARD, 64, 1, 131072, 8, 128, 512, 2048)
+    assert fwd >= 64 * 131072 * 4 + 64 * 2048 * 4 + 64 * 4 * 128 * 512 * 2
+    assert f(dsa.OP_SELECT, 64, 1, 131072, 0, 128, 512, 2048) == ctypes.c_size_t(-1).value
+    assert f(dsa.OP_ATTN, 64, 1, 131072, 8, 0, 512, 2048) == ctypes.c_size_t(-1).value
 
 
 # Fake 16-byte-aligned device addresses: these calls must fail validation on
@@ -98,6 +114,12 @@ def test_topk_rejects_bad_arguments():
     assert f(P, P, 1, 1, 8, 0, 0, None, 0, None) == 1
     assert f(P, P, 1, 1, 8, 4096, 0, None, 0, None) == 2
     assert f(P, P, 1, 2, 8, 4, 7, None, 0, None) == 1
+    # batches of at most 255 rows need a 16-byte-aligned workspace
+    need = dsa.workspace_size(dsa.OP_TOPK, 4, 1, 8, 8, 1, 1, 4)
+    assert need > 0
+    assert f(P, P, 4, 1, 8, 4, 7, None, need, None) == 3
+    assert f(P, P, 4, 1, 8, 4, 7, P, need - 1, None) == 3
+    assert f(P, P, 4, 1, 8, 4, 7, ctypes.c_void_p(0x10008), need, None) == 3
 
 
 def test_attention_rejects_bad_arguments():
@@ -118,10 +140,10 @@ def test_attention_rejects_bad_arguments():
 
 def test_attention_bwd_rejects_bad_arguments():
     f = dsa.lib().dsa_sparse_mla_attn_bwd
-    need = dsa.workspace_size(dsa.OP_ATTN_BWD, 1, 4, 10, 128, 512, 64)
+    need = dsa.workspace_size(dsa.OP_ATTN_BWD, 1, 4, 10, 8, 128, 512, 64)
     # P and dS tiles ([128 heads][32 slots] bf16 each) of every row
     assert need >= 2 * 4 * 2 * 128 * 32 * 2
-    big = dsa.workspace_size(dsa.OP_ATTN_BWD, 1, 4096, 131072, 128, 512, 2048)
+    big = dsa.workspace_size(dsa.OP_ATTN_BWD, 1, 4096, 131072, 8, 128, 512, 2048)
     assert big >= 2 * 2048 * 64 * 128 * 32 * 2  # rows are processed 2048 at a time
 
     def call(H=128, dqk=576, dv=512, k=64, scale=0.04, dt=dsa.BF16, lse=P, dout=P, dq=P, dkv=P,

@@ -45,7 +45,7 @@ def test_forward_graph_replays_match_eager(name, kw):
     print(f"[graph] {name} {kw}", flush=True)
     g = make_inputs(wl, seed=3, device=dev)
     B, T, N = g["q_idx"].shape[0], g["q_idx"].shape[1], g["k_idx"].shape[1]
-    ws = torch.empty(dsa.workspace_size(dsa.OP_FORWARD, B, T, N, wl.H, wl.d_v, wl.k),
+    ws = torch.empty(dsa.workspace_size(dsa.OP_FORWARD, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k),
                      dtype=torch.uint8, device=dev)
 
     def buffers():
