@@ -248,6 +248,34 @@ DSA_API dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It computes exactly what dsa_forward
+ * computes, with the same kernels and checks, and calls no allocating
+ * routine.  Its intermediates live in one fixed array of 128 MiB per device
+ * (DSA_NOALLOC_SCRATCH_BYTES) inside the library, held from the library's
+ * first use on that device until the process ends; a call whose
+ * dsa_workspace_size(DSA_OP_FORWARD, B, T, N, H_I, H, d_v, k) exceeds it
+ * returns DSA_ERR_UNSUPPORTED without launching anything (decode of 64
+ * sequences at 131072 tokens needs 72.3 MiB; batches with a large [B,T,N]
+ * score matrix, e.g. prefill, do not fit).  The array is the one of the
+ * device current at the call, and `stream` must belong to that device
+ * (otherwise DSA_ERR_INVALID_ARG).  Every call on a device shares its array
+ * and leaves its own intermediates there: calls that overlap on one device
+ * (on different streams, or concurrent host threads) race and must be
+ * serialised by the caller.  The kernels clear what they count in, so no
+ * call depends on what an earlier call left.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+DSA_API dsa_status dsa_forward_noalloc(const void* q_idx, const float* q_idx_scale,
+                               const void* k_idx, const float* k_idx_scale,
+                               const float* w, const void* q, const void* kv,
+                               void* out, float* lse, int32_t* idx_out,
+                               int B, int T, int N, int H_I, int d_I, int H, int d_qk, int d_v,
+                               int k, int q_offset, float sm_scale,
+                               dsa_dtype idx_dtype, dsa_dtype attn_dtype, void* stream);
+
+/*
  * Cache append, the step before the path at decode.  Each token keeps its
  * indexer key, in FP8 ("Paper Breakdown: DeepSeek-V3.2", section 2
  * "Architecture: DSA (§2.1)": the indexer runs in FP8), and its latent entry

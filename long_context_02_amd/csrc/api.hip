@@ -4,10 +4,18 @@
 // failures as DSA_ERR_HIP.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "dsa_internal.h"
 
 using namespace dsa;
+
+// Scratch memory of dsa_forward_noalloc, for callers that cannot allocate a
+// workspace: one fixed array per device, held from the library's load on
+// that device until the process ends.  Every dsa_forward_noalloc call on a
+// device uses (and overwrites) that device's array.
+constexpr size_t kNoAllocScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -127,6 +135,74 @@ dsa_status run_attn(const void* q, const void* kv, const int32_t* idx, void* out
                            static_cast<float*>(out), lse, B, T, N, H, d_qk, d_v, k, sm_scale, s);
 }
 
+size_t forward_ws(int B, int T, int N, int H, int d_v, int k) {
+    return align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t)) +
+           attn_ws(B, T, H, d_v, k);
+}
+
+// Argument checks of the fused path; *need receives its workspace bytes.
+dsa_status check_forward(const void* q_idx, const float* q_idx_scale, const void* k_idx,
+                         const float* k_idx_scale, const float* w, const void* q, const void* kv,
+                         const void* out, const float* lse, const int32_t* idx_out, int B, int T,
+                         int N, int H_I, int d_I, int H, int d_qk, int d_v, int k, int q_offset,
+                         float sm_scale, dsa_dtype idx_dtype, dsa_dtype attn_dtype, size_t* need) {
+    // the indexer's output goes to the workspace, so pass a stand-in for the check
+    dsa_status st = check_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w,
+                                  reinterpret_cast<const float*>(16), B, T, N, H_I, d_I, q_offset,
+                                  idx_dtype);
+    if (st != DSA_OK) return st;
+    st = check_attn(q, kv, reinterpret_cast<const int32_t*>(16), out, lse, B, T, N, H, d_qk, d_v, k,
+                    sm_scale, attn_dtype);
+    if (st != DSA_OK) return st;
+    if (idx_out && !aligned16(idx_out)) return DSA_ERR_INVALID_ARG;
+    *need = forward_ws(B, T, N, H, d_v, k);
+    return DSA_OK;
+}
+
+// The fused path on a checked argument set and a workspace of at least
+// forward_ws() bytes: selection, then attention.
+dsa_status run_forward(const void* q_idx, const float* q_idx_scale, const void* k_idx,
+                       const float* k_idx_scale, const float* w, const void* q, const void* kv,
+                       void* out, float* lse, int32_t* idx_out, int B, int T, int N, int H_I,
+                       int d_I, int H, int d_qk, int d_v, int k, int q_offset, float sm_scale,
+                       dsa_dtype idx_dtype, dsa_dtype attn_dtype, void* workspace, hipStream_t s) {
+    char* p = static_cast<char*>(workspace);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p + align_up(select_ws(B, T, N, k)));
+    void* attn_w = p + align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t));
+    dsa_status st = run_select(q_idx, q_idx_scale, k_idx, k_idx_scale, w, idx, B, T, N, H_I, d_I, k,
+                               q_offset, idx_dtype, workspace, s);
+    if (st != DSA_OK) return st;
+    return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, attn_w, s);
+}
+
+// ---- the fixed scratch array of dsa_forward_noalloc ----
+// Device address of `scratch` on each device, looked up once per device
+// (hipGetSymbolAddress with that device current).  In host code the name
+// `scratch` is only a host-side handle of the symbol: kernels and copies get
+// the address looked up here, never the name.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status noalloc_scratch(hipStream_t s, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+    if (s != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return DSA_ERR_HIP;
+        if (sdev != dev) return DSA_ERR_INVALID_ARG;  // the stream must belong to the current device
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return DSA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,9 +229,7 @@ size_t dsa_workspace_size(int op, int B, int T, int N, int H_I, int H, int d_v, 
         case DSA_OP_ATTN: return attn_ws(B, T, H, d_v, k);
         case DSA_OP_SELECT: return select_ws(B, T, N, k);
         case DSA_OP_ATTN_BWD: return attn_bwd_workspace_bytes(B, T, N, k);
-        case DSA_OP_FORWARD:
-            return align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t)) +
-                   attn_ws(B, T, H, d_v, k);
+        case DSA_OP_FORWARD: return forward_ws(B, T, N, H, d_v, k);
         default: return (size_t)-1;
     }
 }
@@ -246,28 +320,36 @@ dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* 
                        int d_I, int H, int d_qk, int d_v, int k, int q_offset, float sm_scale,
                        dsa_dtype idx_dtype, dsa_dtype attn_dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-    // the indexer's output goes to the workspace, so pass a stand-in for the check
-    dsa_status st = check_indexer(q_idx, q_idx_scale, k_idx, k_idx_scale, w,
-                                  reinterpret_cast<const float*>(16), B, T, N, H_I, d_I, q_offset,
-                                  idx_dtype);
+    size_t need = 0;
+    dsa_status st = check_forward(q_idx, q_idx_scale, k_idx, k_idx_scale, w, q, kv, out, lse,
+                                  idx_out, B, T, N, H_I, d_I, H, d_qk, d_v, k, q_offset, sm_scale,
+                                  idx_dtype, attn_dtype, &need);
     if (st != DSA_OK) return st;
-    st = check_attn(q, kv, reinterpret_cast<const int32_t*>(16), out, lse, B, T, N, H, d_qk, d_v, k,
-                    sm_scale, attn_dtype);
-    if (st != DSA_OK) return st;
-    if (idx_out && !aligned16(idx_out)) return DSA_ERR_INVALID_ARG;
-    const size_t need = dsa_workspace_size(DSA_OP_FORWARD, B, T, N, H_I, H, d_v, k);
-    if (need == (size_t)-1) return DSA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
+    return run_forward(q_idx, q_idx_scale, k_idx, k_idx_scale, w, q, kv, out, lse, idx_out, B, T,
+                       N, H_I, d_I, H, d_qk, d_v, k, q_offset, sm_scale, idx_dtype, attn_dtype,
+                       workspace, static_cast<hipStream_t>(stream));
+}
 
-    char* p = static_cast<char*>(workspace);
-    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(p + align_up(select_ws(B, T, N, k)));
-    void* attn_w = p + align_up(select_ws(B, T, N, k)) + align_up((size_t)B * T * k * sizeof(int32_t));
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_select(q_idx, q_idx_scale, k_idx, k_idx_scale, w, idx, B, T, N, H_I, d_I, k, q_offset,
-                    idx_dtype, workspace, s);
+dsa_status dsa_forward_noalloc(const void* q_idx, const float* q_idx_scale, const void* k_idx,
+                               const float* k_idx_scale, const float* w, const void* q,
+                               const void* kv, void* out, float* lse, int32_t* idx_out, int B,
+                               int T, int N, int H_I, int d_I, int H, int d_qk, int d_v, int k,
+                               int q_offset, float sm_scale, dsa_dtype idx_dtype,
+                               dsa_dtype attn_dtype, void* stream) {
+    size_t need = 0;
+    dsa_status st = check_forward(q_idx, q_idx_scale, k_idx, k_idx_scale, w, q, kv, out, lse,
+                                  idx_out, B, T, N, H_I, d_I, H, d_qk, d_v, k, q_offset, sm_scale,
+                                  idx_dtype, attn_dtype, &need);
     if (st != DSA_OK) return st;
-    return run_attn(q, kv, idx, out, lse, B, T, N, H, d_qk, d_v, k, sm_scale, attn_dtype, attn_w, s);
+    if (need > kNoAllocScratchBytes) return DSA_ERR_UNSUPPORTED;  // beyond the fixed scratch array
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    st = noalloc_scratch(s, &ws);
+    if (st != DSA_OK) return st;
+    return run_forward(q_idx, q_idx_scale, k_idx, k_idx_scale, w, q, kv, out, lse, idx_out, B, T,
+                       N, H_I, d_I, H, d_qk, d_v, k, q_offset, sm_scale, idx_dtype, attn_dtype, ws,
+                       s);
 }
 
 dsa_status dsa_cache_append(const float* k_new, const void* kv_new, void* k_cache,

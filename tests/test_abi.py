@@ -213,3 +213,24 @@ def test_indexer_kl_rejects_bad_arguments():
     assert call(ptrs=[P, P, P, P, None], k=0) == 1        # selected slots need k >= 1
     assert call(ptrs=[P, P, P, P, None], k=4096) == 2
     assert call(B=0) == 1
+
+
+def test_forward_noalloc_rejects_before_launching():
+    f = dsa.lib().dsa_forward_noalloc
+    f.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 10 + [ctypes.c_float, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+
+    def call(B=1, T=4, N=8, k=4, q_offset=4, ptrs=None):
+        ptrs = ptrs or [P, P, P, P, P, P, P, P, None, None]
+        return f(*ptrs, B, T, N, 8, 128, 128, 576, 512, k, q_offset, 0.04, dsa.FP8_E4M3FN, dsa.BF16,
+                 None)
+
+    assert call(ptrs=[None, P, P, P, P, P, P, P, None, None]) == 1
+    assert call(q_offset=5) == 1
+    assert call(k=4096) == 2
+    # a [B,T,N] score matrix beyond the fixed 128 MiB array (prefill 8K)
+    assert dsa.workspace_size(dsa.OP_FORWARD, 1, 8192, 8192, 8, 128, 512, 2048) > (128 << 20)
+    assert call(T=8192, N=8192, k=2048, q_offset=0) == 2
+    # decode of 64 sequences at 131072 tokens fits
+    assert dsa.workspace_size(dsa.OP_FORWARD, 64, 1, 131072, 8, 128, 512, 2048) <= (128 << 20)
