@@ -27,7 +27,7 @@ import torch
 E4M3_MAX = 448.0
 
 # tensor ids inside one seed
-_QI, _KI, _W, _Q, _KV, _ROWS = range(6)
+_QI, _KI, _W, _Q, _KV, _ROWS, _QM, _WUK, _WUV = range(9)
 
 
 @dataclass(frozen=True)
@@ -182,4 +182,31 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", chunk_tokens: int = 1
             kv[b, s0:s1] = torch.randn(s1 - s0, wl.d_qk, generator=g, device=dev,
                                        dtype=torch.bfloat16)
     out["kv"] = kv
+    return out
+
+
+# MLA's MHA mode: per-head query width d_n + d_r (nope + rope), per-head
+# value width d_vh, and the up-projections of the d_c-wide latent part.
+MHA_D_N, MHA_D_R, MHA_D_VH = 128, 64, 128
+
+
+def make_mha_inputs(wl: Workload, seed: int = 0, device="cpu"):
+    """Extra inputs of sparse attention in MHA mode for a bf16 workload.
+
+    Returns q_mha [B,T,H,d_n+d_r] ~ N(0,1), w_uk [H,d_n,d_c] and
+    w_uv [H,d_vh,d_c] ~ N(0,1/d_c) (so the up-projected keys and values have
+    unit variance), all bfloat16, with d_c = wl.d_v (the latent width) and
+    sm_scale 1/sqrt(d_n + d_r).  The latent entries are make_inputs()' kv.
+    """
+    dev = torch.device(device)
+    d_c = wl.d_v
+    out = {}
+    g = _gen(dev, seed, _QM)
+    out["q_mha"] = torch.randn(wl.B, wl.T, wl.H, MHA_D_N + MHA_D_R, generator=g, device=dev,
+                               dtype=torch.bfloat16)
+    g = _gen(dev, seed, _WUK)
+    out["w_uk"] = (torch.randn(wl.H, MHA_D_N, d_c, generator=g, device=dev) / math.sqrt(d_c)).to(torch.bfloat16)
+    g = _gen(dev, seed, _WUV)
+    out["w_uv"] = (torch.randn(wl.H, MHA_D_VH, d_c, generator=g, device=dev) / math.sqrt(d_c)).to(torch.bfloat16)
+    out["sm_scale_mha"] = 1.0 / math.sqrt(MHA_D_N + MHA_D_R)
     return out

@@ -27,6 +27,11 @@ Parity status of each function (pins live in ``tests/test_oracle_*.py``):
                                   forward, float64 autograd through torch
                                   SDPA when k >= L, gradient sums
                                   sum_h dq.q = sum_i dc_i.c_i, duplicates)
+  sparse_mha_attention            pinned (absorption identity against the
+                                  MQA-mode oracle; k >= L equals dense causal
+  mha_keys_values                 multi-head attention from torch SDPA with
+                                  per-head keys and values; single index
+                                  gives that head's value row)
   dsa_forward                     pinned (composition; chunked prefill equals
                                   the tail rows of a full prefill)
 """
@@ -40,6 +45,9 @@ from .dsa import (  # noqa: F401
     sparse_mqa_attention_row,
     sparse_mqa_attention_bwd,
     sparse_mqa_attention_bwd_row,
+    mha_keys_values,
+    sparse_mha_attention,
+    sparse_mha_attention_row,
     dsa_forward,
     cache_append,
     indexer_kl,

@@ -218,6 +218,91 @@ def sparse_mqa_attention(q, kv, idx, d_v, sm_scale, rows=None):
 
 
 # --------------------------------------------------------------------------
+# Sparse MLA attention, MHA mode
+# --------------------------------------------------------------------------
+# The DeepSeek-V3.2 paper's section list (page "aipaper.jasonlin.tech",
+# "Sections", "Appendix A MHA and MQA Modes of MLA") names two modes of MLA;
+# DSA runs in MQA mode ("Paper Breakdown: DeepSeek-V3.2", section 2 "DSA
+# under MLA (MQA Mode)").  The appendix body is not on the pages, so MHA mode
+# is read as plain multi-head attention over per-head keys and values
+# up-projected from the same latent entries:
+#     key of token s for head h   = [W_UK[h] c_s[:d_c] ; c_s[d_c:]]
+#     value of token s for head h = W_UV[h] c_s[:d_c]
+# (the rope part c_s[d_c:] is one key part shared by all heads), with per-head
+# queries [q_nope ; q_rope].  W_UK is [H, d_n, d_c] and W_UV [H, d_vh, d_c].
+
+
+def mha_keys_values(kv, w_uk, w_uv, d_c):
+    """Per-head keys [N, H, d_n + d_r] and values [N, H, d_vh] of MHA mode
+    from latent entries kv [N, d_c + d_r] (float64 results)."""
+    C = np.asarray(kv, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    N = C.shape[0]
+    H = w_uk.shape[0]
+    K_nope = np.einsum("hdc,nc->nhd", w_uk, C[:, :d_c])           # W_UK[h] c_s[:d_c]
+    K_rope = np.broadcast_to(C[:, None, d_c:], (N, H, C.shape[1] - d_c))
+    K = np.concatenate([K_nope, K_rope], axis=2)
+    V = np.einsum("hdc,nc->nhd", w_uv, C[:, :d_c])                # W_UV[h] c_s[:d_c]
+    return K, V
+
+
+def sparse_mha_attention_row(q_row, K, V, idx_row, sm_scale):
+    """One query token's attention in MHA mode: head h attends over its own
+    keys K[s, h] and values V[s, h] of the selected tokens s.
+
+    q_row [H, d_n + d_r], K [N, H, d_n + d_r], V [N, H, d_vh], idx_row [k]
+    (-1 or anything outside [0, N) is an empty slot; duplicates count per
+    slot).  Returns (o [H, d_vh], lse [H]); with no valid index o = 0 and
+    lse = -inf.
+    """
+    N, H = K.shape[0], K.shape[1]
+    idx_row = np.asarray(idx_row)
+    sel = idx_row[(idx_row >= 0) & (idx_row < N)]
+    if sel.size == 0:
+        return np.zeros((H, V.shape[2])), np.full(H, -np.inf)
+    o = np.empty((H, V.shape[2]))
+    lse = np.empty(H)
+    for h in range(H):
+        z = sm_scale * (K[sel, h] @ np.asarray(q_row[h], dtype=np.float64))  # [k']
+        m = z.max()
+        p = np.exp(z - m)
+        l = p.sum()
+        o[h] = (p @ V[sel, h]) / l
+        lse[h] = m + math.log(l)
+    return o, lse
+
+
+def sparse_mha_attention(q, kv, w_uk, w_uv, idx, sm_scale, d_c, rows=None):
+    """Sparse MLA attention in MHA mode for all query rows (or ``rows``).
+
+    q [B,T,H,d_n+d_r] per-head queries, kv [B,N,d_c+d_r] latent entries,
+    w_uk [H,d_n,d_c], w_uv [H,d_vh,d_c], idx [B,T,k] (or [len(rows), k]).
+    Returns (out, lse): [B,T,H,d_vh], [B,T,H] or [R,H,d_vh], [R,H].
+    """
+    q = np.asarray(q)
+    kv = np.asarray(kv)
+    idx = np.asarray(idx)
+    B, T, H, _ = q.shape
+    d_vh = np.asarray(w_uv).shape[1]
+    full = rows is None
+    if full:
+        rows = [(b, t) for b in range(B) for t in range(T)]
+    out = np.empty((len(rows), H, d_vh))
+    lse = np.empty((len(rows), H))
+    kvs = {}
+    for r, (b, t) in enumerate(rows):
+        if b not in kvs:
+            kvs = {b: mha_keys_values(kv[b], w_uk, w_uv, d_c)}
+        K, V = kvs[b]
+        irow = idx[b, t] if (full or idx.ndim == 3) else idx[r]
+        out[r], lse[r] = sparse_mha_attention_row(q[b, t], K, V, irow, sm_scale)
+    if full:
+        return out.reshape(B, T, H, d_vh), lse.reshape(B, T, H)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
 # Sparse attention backward (the sparse training stage)
 # --------------------------------------------------------------------------
 # "Paper Breakdown: DeepSeek-V3.2", section 2, "Continued Pre-Training

@@ -229,3 +229,47 @@ def test_attention_bwd_mutants_caught(monkeypatch, golden_dir, kw):
     assert not _fails(BWD_PINS, golden_dir)
     monkeypatch.setattr(od, "sparse_mqa_attention_bwd_row", _bwd_variant(**kw))
     assert _fails(BWD_PINS, golden_dir)
+
+
+# ---- sparse attention, MHA mode
+import test_oracle_mha as tm  # noqa: E402
+
+MHA_PINS = [tm.test_absorption_equals_mqa_mode, tm.test_k_ge_L_equals_dense_causal_mha,
+            tm.test_single_index_gives_that_heads_value_row, tm.test_keys_values_shapes_and_shared_rope]
+_ORIG_KV = od.mha_keys_values
+_ORIG_MHA_ROW = od.sparse_mha_attention_row
+
+
+def _kv_no_rope(kv, w_uk, w_uv, d_c):
+    K, V = _ORIG_KV(kv, w_uk, w_uv, d_c)
+    K = K.copy()
+    K[:, :, w_uk.shape[1]:] = 0.0
+    return K, V
+
+
+def _kv_head0_keys(kv, w_uk, w_uv, d_c):
+    return _ORIG_KV(kv, np.broadcast_to(w_uk[:1], w_uk.shape), w_uv, d_c)
+
+
+def _kv_values_next_head(kv, w_uk, w_uv, d_c):
+    return _ORIG_KV(kv, w_uk, np.roll(w_uv, 1, axis=0), d_c)
+
+
+def _mha_no_scale(q_row, K, V, idx_row, sm_scale):
+    return _ORIG_MHA_ROW(q_row, K, V, idx_row, 1.0)
+
+
+def _mha_drop_duplicates(q_row, K, V, idx_row, sm_scale):
+    return _ORIG_MHA_ROW(q_row, K, V, np.unique(np.asarray(idx_row)), sm_scale)
+
+
+@pytest.mark.parametrize("mutant", [_kv_no_rope, _kv_head0_keys, _kv_values_next_head])
+def test_mha_keys_values_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(od, "mha_keys_values", mutant)
+    assert _fails(MHA_PINS, golden_dir)
+
+
+@pytest.mark.parametrize("mutant", [_mha_no_scale, _mha_drop_duplicates])
+def test_mha_row_mutants_caught(monkeypatch, golden_dir, mutant):
+    monkeypatch.setattr(od, "sparse_mha_attention_row", mutant)
+    assert _fails(MHA_PINS, golden_dir)
