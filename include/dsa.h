@@ -83,7 +83,8 @@ typedef enum dsa_op {
     DSA_OP_ATTN = 1,
     DSA_OP_FORWARD = 2,
     DSA_OP_SELECT = 3,
-    DSA_OP_ATTN_BWD = 4
+    DSA_OP_ATTN_BWD = 4,
+    DSA_OP_ATTN_MHA = 5
 } dsa_op;
 
 /*
@@ -198,6 +199,45 @@ DSA_API dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const 
                                    float* dq, float* dkv,
                                    int B, int T, int N, int H, int d_qk, int d_v, int k,
                                    float sm_scale, dsa_dtype attn_dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse MLA attention in MHA mode (the DeepSeek-V3.2 paper's section list,
+ * page aipaper.jasonlin.tech, "Sections": "Appendix A MHA and MQA Modes of
+ * MLA"; DSA itself runs in MQA mode, dsa_sparse_mla_attn).  Every head h
+ * attends over its own keys and values, up-projected from the same latent
+ * entries c_s = kv[b,s,:] (d_c latent columns, then d_r rope columns):
+ *     key(s, h)   = [W_UK[h] c_s[0:d_c] ; c_s[d_c:d_c+d_r]]     (d_n + d_r)
+ *     value(s, h) = W_UV[h] c_s[0:d_c]                          (d_vh)
+ *     z[h,i]      = sm_scale * q[b,t,h,:] . key(idx[b,t,i], h)
+ *     out[b,t,h,:] = sum_i softmax_i(z[h,:]) * value(idx[b,t,i], h)
+ *     lse[b,t,h]   = log sum_i exp(z[h,i])
+ * After absorbing W_UK into the query and W_UV into the output this is what
+ * MQA mode computes; in MHA mode every selected token costs one key and one
+ * value row per head instead of one shared latent row.
+ *
+ *  q    [B,T,H,d_n+d_r] bf16  per-head queries [q_nope ; q_rope]
+ *  kv   [B,N,d_c+d_r]   bf16  latent entries
+ *  w_uk [H,d_n,d_c]     bf16  key up-projection of each head
+ *  w_uv [H,d_vh,d_c]    bf16  value up-projection of each head
+ *  idx  [B,T,k] int32         as for dsa_sparse_mla_attn (-1 and indices
+ *                             outside [0, N) skipped, duplicates counted)
+ *  out  [B,T,H,d_vh]    bf16  fully overwritten
+ *  lse  [B,T,H] f32 or NULL
+ * Supported: H = 128, d_c = 512, d_r = 64, d_n = 128, d_vh = 128, bf16.
+ * The up-projected keys and values of every latent row of the batch are
+ * computed first (bf16 MFMA, fp32 accumulation, rounded to bf16) into the
+ * workspace (dsa_workspace_size(DSA_OP_ATTN_MHA, B, T, N, 1, H, d_vh, k)
+ * bytes = B*N*H*(192 + 128)*2 rounded up, 16-byte aligned, overwritten);
+ * logits, softmax and accumulation are fp32, the output is rounded to bf16.
+ * The call suits prefill-sized caches: a decode batch would up-project every
+ * cached row of every sequence.
+ */
+DSA_API dsa_status dsa_sparse_mla_attn_mha(const void* q, const void* kv, const void* w_uk,
+                                   const void* w_uv, const int32_t* idx,
+                                   void* out, float* lse,
+                                   int B, int T, int N, int H, int d_c, int d_r, int d_n, int d_vh,
+                                   int k, float sm_scale, dsa_dtype attn_dtype,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -339,6 +379,51 @@ DSA_API dsa_status dsa_indexer_kl(const float* scores, const float* p, const int
  * accept (an unknown op, a size below 1, k above 2048).
  */
 DSA_API size_t dsa_workspace_size(int op, int B, int T, int N, int H_I, int H, int d_v, int k);
+
+/*
+ * Per-kernel timing, a diagnostic (off by default).  dsa_profile_start opens
+ * a window of at most max_launches kernel launches: every kernel the library
+ * launches until dsa_profile_stop records a HIP event on its stream right
+ * before and right after itself.  The events are host-side objects created by
+ * dsa_profile_start (no device memory is allocated); DSA_ERR_INVALID_ARG if a
+ * window is already open or max_launches is outside [1, 2^20].
+ * dsa_profile_stop waits for the recorded events (the only waiting these
+ * two calls do), closes the window and fills out[0..n) with one entry per
+ * distinct kernel (its static name, the number of launches and the summed
+ * event-to-event time in milliseconds); it returns n (<= max_out) or -1 when
+ * no window was open or an event failed.  *dropped (if not NULL) receives
+ * the number of launches beyond max_launches, which were not recorded.  No
+ * library call may run concurrently with dsa_profile_stop, and profiled
+ * calls must not be captured into a graph.
+ */
+typedef struct dsa_kernel_time {
+    const char* name;
+    int launches;
+    double total_ms;
+} dsa_kernel_time;
+DSA_API dsa_status dsa_profile_start(int max_launches);
+DSA_API int dsa_profile_stop(dsa_kernel_time* out, int max_out, int* dropped);
+
+/*
+ * Peak probes, a diagnostic: what this GPU sustains, for comparing kernels
+ * against measured as well as published peaks.  Each runs its probe kernel
+ * five times on `stream`, waits for it, and returns the best rate, or a
+ * negative value on a bad argument or a HIP error.
+ *  DSA_PROBE_STREAM_READ  GB/s of a plain streaming read (16-byte loads,
+ *                         grid-stride) over the first bytes - 64 KiB of buf,
+ *                         a device buffer of bytes >= 1 MiB (16-byte
+ *                         aligned); its last 32 KiB are overwritten
+ *  DSA_PROBE_MFMA_BF16    TFLOP/s of back-to-back v_mfma_f32_16x16x32_bf16
+ *  DSA_PROBE_MFMA_FP8     TFLOP/s of back-to-back
+ *                         v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3)
+ *  DSA_PROBE_MFMA_BF16_32X32  TFLOP/s of back-to-back v_mfma_f32_32x32x16_bf16
+ * The MFMA probes read no memory; buf must be a device pointer to at least
+ * 8 KiB, which they practically never write.  The MFMA rates reflect the
+ * engine clock the chip runs at under that load.
+ */
+enum { DSA_PROBE_STREAM_READ = 0, DSA_PROBE_MFMA_BF16 = 1, DSA_PROBE_MFMA_FP8 = 2,
+       DSA_PROBE_MFMA_BF16_32X32 = 3 };
+DSA_API double dsa_probe_peak(int what, const void* buf, size_t bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 DSA_API const char* dsa_status_string(dsa_status s);

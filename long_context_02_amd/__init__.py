@@ -27,19 +27,24 @@ import torch
 __all__ = [
     "DSAError", "lib", "lib_path", "indexer_scores", "topk_select", "sparse_mla_attn",
     "forward", "indexer_select", "cache_append", "indexer_kl", "workspace_size", "OP_TOPK", "OP_ATTN", "OP_FORWARD",
-    "OP_SELECT", "OP_ATTN_BWD", "sparse_mla_attn_bwd",
+    "OP_SELECT", "OP_ATTN_BWD", "OP_ATTN_MHA", "sparse_mla_attn_bwd", "sparse_mla_attn_mha",
+    "kernel_times", "probe_peaks",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-OP_TOPK, OP_ATTN, OP_FORWARD, OP_SELECT, OP_ATTN_BWD = 0, 1, 2, 3, 4
+OP_TOPK, OP_ATTN, OP_FORWARD, OP_SELECT, OP_ATTN_BWD, OP_ATTN_MHA = 0, 1, 2, 3, 4, 5
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
            3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_BAD_INDEX", 5: "DSA_ERR_HIP"}
 
 _lib = None
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
 
 
 class DSAError(RuntimeError):
@@ -74,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_mla_attn_bwd.argtypes = [vp, vp, i32p, vp, fp, vp, fp, fp, ci, ci, ci, ci, ci, ci, ci,
                                           cf, ci, vp, sz, vp]
     L.dsa_sparse_mla_attn_bwd.restype = ci
+    L.dsa_sparse_mla_attn_mha.argtypes = [vp, vp, vp, vp, i32p, vp, fp, ci, ci, ci, ci, ci, ci, ci, ci,
+                                          ci, cf, ci, vp, sz, vp]
+    L.dsa_sparse_mla_attn_mha.restype = ci
     L.dsa_forward.argtypes = [vp, fp, vp, fp, fp, vp, vp, vp, fp, i32p,
                               ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, sz, vp]
     L.dsa_forward.restype = ci
@@ -85,6 +93,12 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_kl.restype = ci
     L.dsa_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     L.dsa_workspace_size.restype = sz
+    L.dsa_profile_start.argtypes = [ci]
+    L.dsa_profile_start.restype = ci
+    L.dsa_profile_stop.argtypes = [ctypes.POINTER(_KernelTime), ci, ctypes.POINTER(ci)]
+    L.dsa_profile_stop.restype = ci
+    L.dsa_probe_peak.argtypes = [ci, vp, sz, vp]
+    L.dsa_probe_peak.restype = ctypes.c_double
     L.dsa_status_string.argtypes = [ci]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_version.argtypes = []
@@ -266,6 +280,47 @@ def sparse_mla_attn(q, kv, idx, d_v: int, sm_scale: float, out=None, lse: Option
     return out, lse_t
 
 
+def sparse_mla_attn_mha(q, kv, w_uk, w_uv, idx, sm_scale: float, out=None,
+                        lse: Optional[bool] = True, workspace: Optional[torch.Tensor] = None):
+    """Sparse MLA attention in MHA mode (bf16): every head attends over its
+    own keys [W_UK[h] c[:d_c] ; c[d_c:]] and values W_UV[h] c[:d_c] of the
+    selected latent rows.  q [B,T,H,d_n+d_r], kv [B,N,d_c+d_r],
+    w_uk [H,d_n,d_c], w_uv [H,d_vh,d_c], idx [B,T,k] int32.
+    Returns (out [B,T,H,d_vh], lse [B,T,H] or None)."""
+    dev = q.device
+    B, T, H, dq_ = q.shape
+    N, d_lat = kv.shape[1], kv.shape[2]
+    k = idx.shape[-1]
+    d_n, d_c = w_uk.shape[1], w_uk.shape[2]
+    d_vh = w_uv.shape[1]
+    d_r = d_lat - d_c
+    _check("q", q, torch.bfloat16, (B, T, H, dq_), dev)
+    _check("kv", kv, torch.bfloat16, (B, N, d_lat), dev)
+    _check("w_uk", w_uk, torch.bfloat16, (H, d_n, d_c), dev)
+    _check("w_uv", w_uv, torch.bfloat16, (H, d_vh, d_c), dev)
+    _check("idx", idx, torch.int32, (B, T, k), dev)
+    if dq_ != d_n + d_r:
+        raise ValueError(f"q has width {dq_}, expected d_n + d_r = {d_n + d_r}")
+    if out is None:
+        out = torch.empty(B, T, H, d_vh, dtype=torch.bfloat16, device=dev)
+    _check("out", out, torch.bfloat16, (B, T, H, d_vh), dev)
+    lse_t = lse if isinstance(lse, torch.Tensor) else (
+        torch.empty(B, T, H, dtype=torch.float32, device=dev) if lse else None)
+    if lse_t is not None:
+        _check("lse", lse_t, torch.float32, (B, T, H), dev)
+    need = workspace_size(OP_ATTN_MHA, B, T, N, 1, H, d_vh, k) if (1 <= k <= 2048 and H == 128
+                                                                   and d_vh == 128) else 0
+    ws = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = lib().dsa_sparse_mla_attn_mha(_ptr(q), _ptr(kv), _ptr(w_uk), _ptr(w_uv), _ptr(idx),
+                                           _ptr(out), _ptr(lse_t), B, T, N, H, d_c, d_r, d_n, d_vh, k,
+                                           float(sm_scale), BF16, _ptr(ws),
+                                           0 if ws is None else ws.numel() * ws.element_size(),
+                                           _stream(dev))
+    _raise("dsa_sparse_mla_attn_mha", st)
+    return out, lse_t
+
+
 def sparse_mla_attn_bwd(q, kv, idx, out, lse, dout, sm_scale: float, dq=None, dkv=None,
                         workspace: Optional[torch.Tensor] = None):
     """Gradients of sparse MQA attention (bf16).  Takes the forward's inputs,
@@ -398,3 +453,42 @@ def indexer_kl(scores: torch.Tensor, p: torch.Tensor, q_offset: int = 0,
                                   q_offset, _stream(dev))
     _raise("dsa_indexer_kl", st)
     return loss, g
+
+
+def kernel_times(fn, max_launches: int = 8192) -> dict:
+    """Run fn() with the library's per-kernel timing window open (HIP events
+    recorded around every kernel launch on its stream) and return
+    {kernel name: (launches, total milliseconds)}."""
+    L = lib()
+    _raise("dsa_profile_start", L.dsa_profile_start(max_launches))
+    try:
+        fn()
+    finally:
+        entries = (_KernelTime * 64)()
+        dropped = ctypes.c_int(0)
+        n = L.dsa_profile_stop(entries, 64, ctypes.byref(dropped))
+    if n < 0:
+        raise RuntimeError("dsa_profile_stop failed")
+    if dropped.value:
+        raise RuntimeError(f"{dropped.value} launches beyond the timing window of {max_launches}")
+    return {entries[i].name.decode(): (entries[i].launches, entries[i].total_ms) for i in range(n)}
+
+
+def probe_peaks(device=None, read_mib: int = 2048) -> dict:
+    """What this GPU sustains: a streaming read over read_mib MiB (GB/s) and
+    back-to-back bf16 and FP8 MFMAs (TFLOP/s), from the library's probes."""
+    dev = torch.device(device or "cuda")
+    buf = torch.empty(read_mib << 20, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    L = lib()
+    with torch.cuda.device(dev):
+        s = _stream(dev)
+        res = {"stream_read_gbs": L.dsa_probe_peak(0, _ptr(buf), buf.numel(), s),
+               "mfma_bf16_tflops": L.dsa_probe_peak(1, _ptr(buf), buf.numel(), s),
+               "mfma_fp8_tflops": L.dsa_probe_peak(2, _ptr(buf), buf.numel(), s),
+               "mfma_bf16_32x32_tflops": L.dsa_probe_peak(3, _ptr(buf), buf.numel(), s)}
+    del buf
+    for k, v in res.items():
+        if v < 0:
+            raise RuntimeError(f"dsa_probe_peak failed for {k}")
+    return {k: round(v, 1) for k, v in res.items()}

@@ -229,6 +229,9 @@ size_t dsa_workspace_size(int op, int B, int T, int N, int H_I, int H, int d_v, 
         case DSA_OP_ATTN: return attn_ws(B, T, H, d_v, k);
         case DSA_OP_SELECT: return select_ws(B, T, N, k);
         case DSA_OP_ATTN_BWD: return attn_bwd_workspace_bytes(B, T, N, k);
+        case DSA_OP_ATTN_MHA:
+            if (H != 128 || d_v != 128) return (size_t)-1;
+            return attn_mha_workspace_bytes(B, N);
         case DSA_OP_FORWARD: return forward_ws(B, T, N, H, d_v, k);
         default: return (size_t)-1;
     }
@@ -312,6 +315,32 @@ dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const int32_t*
         if (st != DSA_OK) return st;
     }
     return launch_attn_bwd_bf16(q, kv, idx, out, lse, dout, dq, dkv, B, T, N, k, sm_scale, workspace, s);
+}
+
+dsa_status dsa_sparse_mla_attn_mha(const void* q, const void* kv, const void* w_uk,
+                                   const void* w_uv, const int32_t* idx, void* out, float* lse,
+                                   int B, int T, int N, int H, int d_c, int d_r, int d_n, int d_vh,
+                                   int k, float sm_scale, dsa_dtype attn_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!q || !kv || !w_uk || !w_uv || !idx || !out) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(idx) ||
+        !aligned16(out) || (lse && !aligned16(lse)))
+        return DSA_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || N < 1 || k < 1) return DSA_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale)) return DSA_ERR_INVALID_ARG;
+    if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+    if (attn_dtype != DSA_BF16) return attn_dtype == DSA_F32 || attn_dtype == DSA_FP8_E4M3FN
+                                           ? DSA_ERR_UNSUPPORTED : DSA_ERR_INVALID_ARG;
+    if (H != 128 || d_c != 512 || d_r != 64 || d_n != 128 || d_vh != 128) return DSA_ERR_UNSUPPORTED;
+    if ((long long)B * T > 0x7fffffffLL || (long long)B * N >= (1LL << 31)) return DSA_ERR_UNSUPPORTED;
+    const size_t need = attn_mha_workspace_bytes(B, N);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validation_enabled()) {
+        const dsa_status st = validate_indices(idx, (size_t)B * T * k, N, s);
+        if (st != DSA_OK) return st;
+    }
+    return launch_attn_mha_bf16(q, kv, w_uk, w_uv, idx, out, lse, B, T, N, k, sm_scale, workspace, s);
 }
 
 dsa_status dsa_forward(const void* q_idx, const float* q_idx_scale, const void* k_idx,

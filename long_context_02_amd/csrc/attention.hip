@@ -33,6 +33,8 @@
 // with fewer rows than CUs split the slots over several workgroups; each
 // writes its O rows normalised in bf16 with its per-head (max, exp-sum), and
 // attn_combine merges them.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace dsa {
@@ -49,22 +51,58 @@ constexpr int SLOTS = 2048;              // max index slots per workgroup
 constexpr float REF_GAP = 64.0f;         // max log2 gap above the reference max
 constexpr int DMA_PER_TILE = 9;          // direct-to-LDS loads per wave and tile
 
-template <bool PARTIAL>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The key product's accumulator chain in VGPRs.  With the whole AGPR file
+// holding the 32 x 512 fp32 output accumulator, the compiler would otherwise
+// give this chain AGPRs too (every MFMA gets the AGPR form when a kernel
+// uses AGPRs) and shuttle output blocks between the two register files.
+// first: D = A B (no accumulator read); next: D += A B (the back-to-back
+// dependent accumulation the MFMA pipe forwards); last: D += A B followed by
+// 24 wait states before any other instruction may read D (an XDL result read
+// by VALU or memory instructions needs up to passes + 3 = 19 of them).
+__device__ __forceinline__ void qk_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next(f32x16& d, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(d)
+                 : "v"(a), "v"(b));
+}
+
+// LDS layout of a gathered tile: latent row r (1 KiB) keeps its 16-byte
+// chunk c in slot c ^ lat_swz(r); the rope parts (128 B per row) follow the
+// 32 latent rows, chunk c of row r in slot c ^ rope_swz(r).
+//  * key-fragment reads (ds_read_b128, 16 lanes per pass): 16 consecutive
+//    rows at one chunk -- lat_swz is a permutation of 0..15 on any 16
+//    consecutive rows, and rope_swz on rows of one parity;
+//  * transposed value reads (ds_read_b64_tr_b16, 32 lanes per pass): 4
+//    consecutive rows x 4 consecutive chunks -- lat_swz gives the 4 rows
+//    different multiples of 4.
+// Both land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int lat_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
+
+template <bool PARTIAL, bool NEG>
 __global__ __launch_bounds__(NTA) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml, int T, int N, int k, int nsplit, int slots_per_split,
     float scale_log2) {
-    // four ring stages, separate objects so that the compiler can tell the
-    // stage being read from the stages being filled
-    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
-    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + 3 * TK];
+    // four ring stages; tile t lives in stage t % 4
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * STAGE];
+    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + 4 * TK];
     __shared__ int s_last;
     __shared__ int s_redo;
+    __shared__ unsigned s_notfull[(SLOTS + 4 * TK) / TK / 32 + 1];  // tiles with an invalid slot
 
     // (split batches only: causal prefill rows differ in length, and giving
     // each XCD a contiguous range of them would unbalance the XCDs)
@@ -73,43 +111,45 @@ void sparse_mla_attn_bf16(
     const size_t row = item / (unsigned)nsplit;
     const int b = (int)(row / (unsigned)T);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int m = lane & 15, g = lane >> 4;
+    // 32x32 MFMA lane roles: column hl (a head, a key row or a value column),
+    // half hh (which 8 of the 16 k indices the lane holds)
+    const int hl = lane & 31, hh = lane >> 5;
     const int slot0 = split * slots_per_split;
     const int nslots = max(0, min(k - slot0, slots_per_split));
     const uint16_t* __restrict__ kv_b = kv + (size_t)b * N * DQK;
 
     // ---- slot indices of this workgroup; the last valid one
     if (tid == 0) s_last = -1;
+    if (tid < (SLOTS + 4 * TK) / TK / 32 + 1) s_notfull[tid] = 0;
     __syncthreads();
     int my_last = -1;
     const int nslots_pad = (nslots + TK - 1) / TK * TK;
-    // this wave's 32 query heads (two blocks of 16) as B operands
-    bf16x8 qf[2][DQK / 32];
+    // this wave's 32 query heads as B operands: lane (hl, hh) holds head
+    // 32*wave + hl, features 16*ks + 8*hh .. +7
+    bf16x8 qf[DQK / 16];
     {
         // all of a thread's index loads are issued before the first is
         // waited for (a loop that stores each index as it arrives waits for
         // one memory round trip per iteration), and Q's loads right behind
         // them, so that Q arrives while the indices are used
-        constexpr int PER = (SLOTS + 3 * TK + NTA - 1) / NTA;
+        constexpr int PER = (SLOTS + 4 * TK + NTA - 1) / NTA;
         int id[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = tid + j * NTA;
             id[j] = i < nslots ? idx[row * k + slot0 + i] : -1;
         }
+        const uint16_t* qh = q + (row * H + 32 * wave + hl) * DQK + 8 * hh;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const uint16_t* qh = q + (row * H + 32 * wave + 16 * hb + m) * DQK + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < DQK / 32; ++ks)
-                qf[hb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 32 * ks));
-        }
+        for (int ks = 0; ks < DQK / 16; ++ks)
+            qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 16 * ks));
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = tid + j * NTA;
-            if (i < nslots_pad + 3 * TK) {
+            if (i < nslots_pad + 4 * TK) {
                 sidx[i] = id[j];
                 if (id[j] >= 0 && id[j] < N) my_last = i;
+                else if (i < nslots_pad) atomicOr(&s_notfull[i / (32 * TK)], 1u << ((i / TK) & 31));
             }
         }
     }
@@ -122,53 +162,61 @@ void sparse_mla_attn_bf16(
     const int dummy = last >= 0 ? sidx[last] : 0;
 
     // Softmax without rescaling the accumulator: the reference max m_ref of
-    // head 16*hb + m is the max of the first tile with a valid key, and
+    // the lane's head is the max of the first tile with a valid key, and
     // later exponentials exp2(x - m_ref) may grow up to 2^REF_GAP, which fp32
     // accumulators and bf16 weights hold without loss of relative precision.
     // A tile that exceeds the reference by more than REF_GAP flags the
     // workgroup, which then reruns the pass with m_ref = the exact max it
     // recorded (so every exponential is <= 1).
-    f32x4 o[2][DV / 16];
-    float m_ref[2], m_all[2], l_part[2];
+    f32x16 o[DV / 32];
+    float m_ref = -__builtin_inff(), m_all = -__builtin_inff(), l_part = 0.f;
     bool over = false;
     if (tid == 0) s_redo = 0;
 
-    // per-lane LDS offsets inside a stage (all rows use the same swizzle of
-    // their low four bits, so these hold for every tile).  QK^T: chunk
-    // 4*ks + g of row r sits in slot 4*(ks ^ (swz>>2)) + (g ^ (swz&3)).
-    int qk_off[4];
+    // Per-lane LDS offsets inside a stage (the same for every tile).
+    // Key fragment of step ks (A operand: key row hl, features 16ks + 8hh):
+    // latent chunk 2ks + hh (ks < 32) in slot (2ks + hh) ^ lat_swz(hl)
+    // = 256*(ks/8) + 32*((ks%8) ^ (f>>1)) + 16*((hh ^ f) & 1); rope chunk
+    // 2(ks-32) + hh (ks >= 32) in slot (2(ks-32) + hh) ^ rope_swz(hl).
+    int k_off[8], r_off[4];
     {
-        const int sw = swz(m);
+        const int f = lat_swz(hl), fr = rope_swz(hl);
 #pragma unroll
-        for (int b2 = 0; b2 < 4; ++b2)
-            qk_off[b2] = m * LAT + 16 * (4 * (b2 ^ (sw >> 2)) + (g ^ (sw & 3)));
+        for (int j = 0; j < 8; ++j) k_off[j] = hl * LAT + 16 * ((2 * j + hh) ^ f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r_off[j] = TK * LAT + hl * ROPE + 16 * ((2 * j + hh) ^ fr);
     }
-    // rope chunk 4*a + g (a = 0, 1) of row r sits in slot (4*a + g) ^ (r % 8)
-    int rope_off[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) rope_off[a] = TK * LAT + m * ROPE + 16 * ((4 * a + g) ^ (m & 7));
-    // P V: the K order of the MFMA is {4g..4g+3, 16+4g..16+4g+3} on both
-    // operands.  V comes from the latent rows by transposed reads: lane m of
-    // group g reads 8 bytes of row r = 4g + m/4 (and r + 16) at columns
-    // 16*nv + 4*(m%4), i.e. chunk 2*nv + (m%4)/2, and receives column
-    // 16*nv + m of those four rows.  Slot (2*nv + ch) ^ swz(r) splits into
-    // 32*((nv%8) ^ (swz>>1)) + 16*(ch ^ (swz&1)) + 256*(nv/8).
-    // (row r + 16 has the same swizzle, 16 KiB further on)
-    int tr_off[8];
+    // Value fragment of k step kk and column block nb (B operand: column
+    // 32nb + hl, the eight keys of half hh in the order the S^T accumulator
+    // holds them: 16kk + 4hh + {0..3}, then 16kk + 8 + 4hh + {0..3}).  Two
+    // transposed reads: in each 16-lane group g (= 2hh + gc), lane m reads 8
+    // bytes of row 16kk + 8j + 4hh + m/4 at columns 32nb + 16gc + 4(m%4),
+    // i.e. chunk 4nb + 2gc + (m%4)/2, and receives column 32nb + 16gc + m of
+    // the four rows.  lat_swz of those rows is 4(m/4) + ((2j + hh) & 3),
+    // independent of kk; slot = 16*(nb/4) + ((4(nb%4) + 2gc + (m%4)/2) ^ f).
+    int v_off[2][4];
     {
-        const int r = 4 * g + (m >> 2);
-        const int sw = swz(r), ch = (m & 3) >> 1;
+        const int m = lane & 15, gc = (lane >> 4) & 1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            tr_off[j] = r * LAT + 32 * (j ^ (sw >> 1)) + 16 * (ch ^ (sw & 1)) + 8 * (m & 1);
+        for (int j = 0; j < 2; ++j) {
+            const int r = 8 * j + 4 * hh + (m >> 2);
+            const int f = lat_swz(r);
+#pragma unroll
+            for (int nq = 0; nq < 4; ++nq)
+                v_off[j][nq] = r * LAT + 16 * ((4 * nq + 2 * gc + ((m & 3) >> 1)) ^ f) + 8 * (m & 1);
+        }
     }
+    const unsigned ring_base = lds_addr(ring);
+    auto stage_of = [&](int tile) __attribute__((always_inline)) -> const uint8_t* {
+        return ring + (tile & 3) * STAGE;
+    };
 
     // direct-to-LDS gather of one tile: wave w brings latent rows 8w..8w+7
-    // (one 1 KiB row per instruction, lane l fetching chunk l ^ swz(r)) and
-    // the rope parts of rows 8w..8w+7 (lane l: row 8w+l/8, chunk
-    // (l%8) ^ (row%8)); 9 loads per wave and tile.  The loads go through a
-    // buffer resource over this sequence's rows (the base stays in SGPRs;
-    // the row offset of a latent load is a scalar).  A tile at or past
+    // (one 1 KiB row per instruction, lane l fetching chunk l ^ lat_swz(r))
+    // and the rope parts of rows 8w..8w+7 (lane l: row 8w+l/8, chunk
+    // (l%8) ^ rope_swz(row)); 9 loads per wave and tile.  The loads go
+    // through a buffer resource over this sequence's rows (the base stays in
+    // SGPRs; the row offset of a latent load is a scalar).  A tile at or past
     // n_tiles is still "loaded", with offsets beyond the resource's range:
     // such loads touch no memory, so every tile issues the same number of
     // loads and the ring's wait counts do not depend on the position.
@@ -177,7 +225,7 @@ void sparse_mla_attn_bf16(
     const i32x4 kv_rsrc = buffer_rsrc(kv_b, (unsigned)N * (unsigned)(2 * DQK));
     const int lane16 = lane << 4;
     auto gather_id = [&](int tile) __attribute__((always_inline)) {
-        // (the lookahead reaches three tiles past the last one: sidx holds
+        // (the lookahead reaches four tiles past the last one: sidx holds
         // -1 there, and such tiles are never gathered)
         const int r = 8 * wave + (lane >> 3);
         int id = sidx[tile * TK + r];
@@ -185,225 +233,258 @@ void sparse_mla_attn_bf16(
         return tile < n_tiles ? id : -1;
     };
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    auto dma = [&](uint8_t* st, int id, int u) __attribute__((always_inline)) {
+    auto dma = [&](int tile, int id, int u) __attribute__((always_inline)) {
+        const unsigned st = ring_base + (unsigned)((tile & 3) * STAGE);
         if (u < 8) {
             const int ru = 8 * wave_s + u;
             const int idu = __builtin_amdgcn_readlane(id, 8 * u);
-            const unsigned vo = idu < 0 ? 0x80000000u : (unsigned)(lane16 ^ (swz(ru) << 4));
-            load_lds16(kv_rsrc, lds_addr(st) + ru * LAT, vo, (unsigned)max(idu, 0) * (2 * DQK));
+            const unsigned vo = idu < 0 ? 0x80000000u : (unsigned)(lane16 ^ (lat_swz(ru) << 4));
+            load_lds16(kv_rsrc, st + ru * LAT, vo, (unsigned)max(idu, 0) * (2 * DQK));
         } else {
             const int r = 8 * wave + (lane >> 3);
             const unsigned vo = id < 0 ? 0x80000000u
-                                       : (unsigned)id * (2 * DQK) + 1024 + 16 * ((lane & 7) ^ (r & 7));
-            load_lds16(kv_rsrc, lds_addr(st) + TK * LAT + wave_s * 1024, vo, 0u);
+                                       : (unsigned)id * (2 * DQK) + 1024 + 16 * ((lane & 7) ^ rope_swz(r));
+            load_lds16(kv_rsrc, st + TK * LAT + wave_s * 1024, vo, 0u);
         }
     };
-    auto issue = [&](uint8_t* st, int tile) __attribute__((always_inline)) {
+    auto issue = [&](int tile) __attribute__((always_inline)) {
         const int id = gather_id(tile);
 #pragma unroll
-        for (int u = 0; u < DMA_PER_TILE; ++u) dma(st, id, u);
+        for (int u = 0; u < DMA_PER_TILE; ++u) dma(tile, id, u);
+    };
+    // (the per-lane address parts go through an empty asm statement at each
+    // use, so that the compiler computes every address next to its read --
+    // two VALU operations -- instead of keeping one register per step)
+    auto kfrag = [&](const uint8_t* st, int ks) __attribute__((always_inline)) -> bf16x8 {
+        const uint8_t* p = ks < 32 ? st + k_off[ks & 7] + 256 * (ks >> 3) : st + r_off[ks - 32];
+        return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+    };
+    // a tile barrier that is also a compiler memory barrier (no LDS access
+    // moves across it) but, unlike __syncthreads(), waits for no global loads
+    // (its own earlier LDS reads are finished first, so no stage a wave is
+    // still reading gets refilled)
+    auto tile_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
-    // Multiply tile `tile` (in stage st); when nxt is not null, the loads of
-    // tile `tile + 3` into nxt are spread over the QK^T steps.
-    auto compute = [&](const uint8_t* st, int tile, uint8_t* nxt) __attribute__((always_inline)) {
-        const int nid = gather_id(tile + 3);
-        // validity of this lane's keys 4g..4g+3 and 16+4g..16+4g+3
-        const int4 ia = *reinterpret_cast<const int4*>(&sidx[tile * TK + 4 * g]);
-        const int4 ib = *reinterpret_cast<const int4*>(&sidx[tile * TK + 16 + 4 * g]);
-
-        // S^T[key, head] for keys 16*nb + 4*g + i, heads 16*hb + m.  Both key
-        // blocks advance together (four independent accumulators); fragments
-        // are loaded two k-steps ahead of the MFMAs that use them.
-        f32x4 sacc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
-                            {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
-        auto kfrag = [&](int nb, int ks) __attribute__((always_inline)) -> bf16x8 {
-            const uint8_t* p = ks < 16 ? st + nb * 16 * LAT + qk_off[ks & 3] + 256 * (ks >> 2)
-                                       : st + rope_off[ks - 16] + nb * 16 * ROPE;
-            return as_bf16x8(*reinterpret_cast<const uint4*>(p));
-        };
-        bf16x8 kf[3][2];
-        kf[0][0] = kfrag(0, 0); kf[0][1] = kfrag(1, 0);
-        kf[1][0] = kfrag(0, 1); kf[1][1] = kfrag(1, 1);
+    // S^T of tile `tile` into sacc; the loads of tile `tile + 2` are spread
+    // over its steps.  Register i of the accumulator holds key
+    // 8(i/4) + 4hh + i%4 of head hl.
+    auto qk = [&](int tile, f32x16& sacc) __attribute__((always_inline)) {
+        const uint8_t* st = stage_of(tile);
+        const int nid = gather_id(tile + 2);
+        // two accumulator chains (even and odd steps): a dependent MFMA waits
+        // for its predecessor's result, so one chain would run the MFMA
+        // pipe at about two thirds of its rate
+        f32x16 s_odd;
+        constexpr int KD = 2;  // prefetch distance
+        bf16x8 kf[KD + 1];
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) kf[ks] = kfrag(st, ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-            const int c = ks % 3;
-            if (ks + 2 < 18) {
-                kf[(ks + 2) % 3][0] = kfrag(0, ks + 2);
-                kf[(ks + 2) % 3][1] = kfrag(1, ks + 2);
-            }
-            sacc[0][0] = mfma_bf16(kf[c][0], qf[0][ks], sacc[0][0]);
-            sacc[0][1] = mfma_bf16(kf[c][0], qf[1][ks], sacc[0][1]);
-            sacc[1][0] = mfma_bf16(kf[c][1], qf[0][ks], sacc[1][0]);
-            sacc[1][1] = mfma_bf16(kf[c][1], qf[1][ks], sacc[1][1]);
-            if ((ks & 1) == 0) dma(nxt, nid, ks >> 1);  // loads 0..8 at the even steps
+        for (int ks = 0; ks < DQK / 16; ++ks) {
+            if (ks + KD < DQK / 16) kf[(ks + KD) % (KD + 1)] = kfrag(st, ks + KD);
+            f32x16& acc = (ks & 1) ? s_odd : sacc;
+            const bf16x8& kcur = kf[ks % (KD + 1)];
+            if (ks < 2) qk_first(acc, kcur, qf[ks]);
+            else if (ks + 1 < DQK / 16) qk_next(acc, kcur, qf[ks]);
+            else qk_last(acc, kcur, qf[ks]);
+            if ((ks & 3) == 0) dma(tile + 2, nid, ks >> 2);  // loads 0..8 at steps 0, 4, .., 32
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] += s_odd[i];
+    };
 
-        const int ids[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
-        bool ok[8];
+    // Softmax of tile `tile` (S^T in s, turned into the weights in place),
+    // in NS pieces so that it can run in the shadow of other work; piece j of
+    // NS = 20 after each call of step(j).  The weights end up as bf16 A
+    // operands in pa (k step kk = accumulator registers 8kk .. 8kk+7).
+    // Softmax of tile `tile` (S^T in s, turned into the weights in place), in
+    // pieces so that it can run in the shadow of other work.  The max runs
+    // over all 32 raw logits: a slot that is not valid gathered the dummy
+    // row, the last valid row of this workgroup, so its logit repeats one of
+    // the valid ones and the max is that of the valid slots, exactly.  With
+    // a non-negative scale max(s * scale) = max(s) * scale (s * scale is
+    // monotonic in s; NEG: -max(-s) * scale for a negative one); each weight
+    // is exp2(fma(s, scale, -m)), and the weights of slots that are not valid
+    // are set to 0.  Only tiles with an invalid slot read the slot indices.
+    struct Soft {
+        unsigned okm;
+        float mx, mr;
+    };
+    auto soft_begin = [&](int tile, Soft& sf) __attribute__((always_inline)) {
+        sf.mx = -__builtin_inff();
+        sf.mr = 0.f;
+        unsigned okm = 0xffffu;
+        if ((s_notfull[tile >> 5] >> (tile & 31)) & 1u) {
+            // validity of this lane's keys 8j + 4hh + {0..3}, j = 0..3, as a mask
+            okm = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ok[i] = (unsigned)ids[i] < (unsigned)N;
-        bf16x8 pa[2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            // x = s * scale in base 2 (-inf for invalid slots); products are
-            // never signalling NaNs, so the maxima need no canonicalisation
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = ok[i] ? sacc[i >> 2][hb][i & 3] * scale_log2 : -__builtin_inff();
-            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            // per-lane bookkeeping; the max over the head's four lane groups is
-            // only needed to fix the reference on the first tile with a valid key
-            if (m_ref[hb] == -__builtin_inff()) {
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                m_ref[hb] = mx;  // O and l are still 0
+            for (int j = 0; j < 4; ++j) {
+                const int4 iv = *reinterpret_cast<const int4*>(&sidx[tile * TK + 8 * j + 4 * hh]);
+                okm |= ((unsigned)iv.x < (unsigned)N ? 1u : 0u) << (4 * j);
+                okm |= ((unsigned)iv.y < (unsigned)N ? 1u : 0u) << (4 * j + 1);
+                okm |= ((unsigned)iv.z < (unsigned)N ? 1u : 0u) << (4 * j + 2);
+                okm |= ((unsigned)iv.w < (unsigned)N ? 1u : 0u) << (4 * j + 3);
             }
-            m_all[hb] = fmaxf(m_all[hb], mx);
-            over |= mx > m_ref[hb] + REF_GAP;
-            // exp2(-inf - m) = 0 for invalid slots; a head with no valid key so
-            // far (m_ref = -inf) subtracts 0 instead, so its weights stay 0.
+        }
+        sf.okm = okm;
+    };
+    auto soft_piece = [&](int j, f32x16& sv, Soft& sf, bf16x8* pa) __attribute__((always_inline)) {
+        if (j < 8) {
+            // products are never signalling NaNs, so the maxima need no
+            // canonicalisation
+            sf.mx = NEG ? fmaxf(sf.mx, fmaxf(-sv[2 * j], -sv[2 * j + 1]))
+                        : fmaxf(sf.mx, fmaxf(sv[2 * j], sv[2 * j + 1]));
+        } else if (j == 8) {
+            // per-lane bookkeeping; the head's max over both lane halves is
+            // only needed to fix the reference on the first tile
+            float mx = NEG ? sf.mx * -scale_log2 : sf.mx * scale_log2;
+            if (m_ref == -__builtin_inff()) {
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                m_ref = mx;  // O and l are still 0
+            }
+            m_all = fmaxf(m_all, mx);
+            over |= mx > m_ref + REF_GAP;
             // v_exp_f32 without range reduction: the argument is at most
             // REF_GAP (larger ones make the pass rerun) and results below the
             // normal range flush to 0, which the weights can afford.
-            const float mr = m_ref[hb] == -__builtin_inff() ? 0.f : m_ref[hb];
-            float p[8];
+            sf.mr = m_ref;
+        } else if (j < 17) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
-                l_part[hb] += p[i];
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * (j - 9) + e;
+                const float pw = __builtin_amdgcn_exp2f(fmaf(sv[i], scale_log2, -sf.mr));
+                sv[i] = (sf.okm >> i) & 1u ? pw : 0.f;
+                l_part += sv[i];
             }
-            pa[hb] = bf16x8{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                            (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+        } else if (j < 19) {
+            const int kk = j - 17;
+            pa[kk] = bf16x8{(__bf16)sv[8 * kk + 0], (__bf16)sv[8 * kk + 1], (__bf16)sv[8 * kk + 2],
+                            (__bf16)sv[8 * kk + 3], (__bf16)sv[8 * kk + 4], (__bf16)sv[8 * kk + 5],
+                            (__bf16)sv[8 * kk + 6], (__bf16)sv[8 * kk + 7]};
         }
-        // P V, V fragments read two steps ahead
-        auto vfrag = [&](int nv) __attribute__((always_inline)) -> bf16x8 {
-            const int j = nv & 7, hi = 256 * (nv >> 3);
-            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + tr_off[j] + hi));
-            const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(st + tr_off[j] + hi + 16 * LAT));
+    };
+
+    // O[head, v] += P V over tile `tile` (weights pa); when SOFT, the pieces
+    // of the next tile's softmax (on sn, into pn) run between the MFMAs.
+    // Value fragments are read three steps ahead.
+    auto pv = [&](int tile, const bf16x8* pa, auto soft_t, f32x16& sn, Soft& sf, bf16x8* pn)
+        __attribute__((always_inline)) {
+        constexpr bool SOFT = decltype(soft_t)::value;
+        const uint8_t* st = stage_of(tile);
+        auto vfrag = [&](int s) __attribute__((always_inline)) -> bf16x8 {
+            const int kk = s >> 4, nb = s & 15;
+            const uint8_t* base = st + kk * 16 * LAT + 256 * (nb >> 2);
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[0][nb & 3]));
+            const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[1][nb & 3]));
             const uint4 vv = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 0, 1)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 2, 3))};
             return as_bf16x8(vv);
         };
-        bf16x8 vf[3];
-        vf[0] = vfrag(0);
-        vf[1] = vfrag(1);
+        constexpr int VD = 2;  // prefetch distance
+        bf16x8 vf[VD + 1];
+#pragma unroll
+        for (int s = 0; s < VD; ++s) vf[s] = vfrag(s);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nv = 0; nv < DV / 16; ++nv) {
-            if (nv + 2 < DV / 16) vf[(nv + 2) % 3] = vfrag(nv + 2);
-            o[0][nv] = mfma_bf16(pa[0], vf[nv % 3], o[0][nv]);
-            o[1][nv] = mfma_bf16(pa[1], vf[nv % 3], o[1][nv]);
+        for (int s = 0; s < 2 * (DV / 32); ++s) {
+            if (s + VD < 2 * (DV / 32)) vf[(s + VD) % (VD + 1)] = vfrag(s + VD);
+            o[s & 15] = mfma32(pa[s >> 4], vf[s % (VD + 1)], o[s & 15]);
+            if (SOFT && s < 19) soft_piece(s, sn, sf, pn);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // one ring step: wait for tile `it` (the loads of tiles it+1 and it+2 may
-    // stay in flight), publish it with a barrier (which also tells every wave
-    // that the stage read at it-1 is free), then multiply tile it while
-    // refilling that stage with tile it+3
-    auto step = [&](uint8_t* cur, uint8_t* nxt, int it) __attribute__((always_inline)) {
-        if (it >= n_tiles) return;
-        DSA_WAIT_VM(2 * DMA_PER_TILE);
-        // a barrier that is also a compiler memory barrier (no LDS access moves
-        // across it) but, unlike __syncthreads(), waits for no global loads
-        // (its own earlier LDS reads are finished first, so no stage a
-        // wave is still reading gets refilled)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        compute(cur, it, nxt);
-    };
-
-    // the first pass's ring prologue; then all of Q (k = 8*(l/16)+j within
-    // each 32-wide step of d, loaded with the slot indices) is in registers
-    // before the loop: the waits the compiler would otherwise place at Q's
-    // first uses inside the loop would also wait for the gather loads it
-    // does not know about
-    issue(st0, 0);
-    issue(st1, 1);
-    issue(st2, 2);
+    // the first pass's ring prologue; then all of Q (loaded with the slot
+    // indices) is in registers before the loop: the waits the compiler would
+    // otherwise place at Q's first uses inside the loop would also wait for
+    // the gather loads it does not know about
+    issue(0);
+    issue(1);
     DSA_WAIT_VM(0);
 
+    // Pipeline of a pass: tile t's S^T on the MFMA pipe; then tile t-1's
+    // P V on the MFMA pipe with tile t's softmax on the VALU in its shadow.
+    // Tile t + 2 is gathered during tile t's S^T into the stage of tile t-2,
+    // which every wave has finished with at tile t's barrier.
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
+        for (int i = 0; i < DV / 32; ++i)
 #pragma unroll
-            for (int i = 0; i < DV / 16; ++i) o[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            l_part[hb] = 0.f;
-            m_ref[hb] = pass == 0 ? -__builtin_inff() : m_all[hb];
-            if (pass == 0) m_all[hb] = -__builtin_inff();
-        }
+            for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+        l_part = 0.f;
+        m_ref = pass == 0 ? -__builtin_inff() : m_all;
+        if (pass == 0) m_all = -__builtin_inff();
         if (pass == 1) {
-            issue(st0, 0);
-            issue(st1, 1);
-            issue(st2, 2);
+            issue(0);
+            issue(1);
         }
-        for (int it = 0; it < n_tiles; it += 4) {
-            step(st0, st3, it);
-            step(st1, st0, it + 1);
-            step(st2, st1, it + 2);
-            step(st3, st2, it + 3);
+        if (n_tiles > 0) {
+            f32x16 s;
+            Soft sf;
+            bf16x8 pa[2], pn[2];
+            // tile 0 (tile 1's loads may stay in flight)
+            DSA_WAIT_VM(DMA_PER_TILE);
+            tile_barrier();
+            qk(0, s);
+            soft_begin(0, sf);
+#pragma unroll
+            for (int j = 0; j < 19; ++j) soft_piece(j, s, sf, pa);
+            for (int it = 1; it < n_tiles; ++it) {
+                DSA_WAIT_VM(DMA_PER_TILE);
+                tile_barrier();
+                qk(it, s);
+                soft_begin(it, sf);
+                pv(it - 1, pa, std::true_type{}, s, sf, pn);
+                pa[0] = pn[0];
+                pa[1] = pn[1];
+            }
+            pv(n_tiles - 1, pa, std::false_type{}, s, sf, pn);
         }
         DSA_WAIT_VM(0);  // the loads past the last tile land before the stages are reused
         if (pass == 1) break;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {  // per-lane maxima -> max of the head
-            m_all[hb] = fmaxf(m_all[hb], __shfl_xor(m_all[hb], 16, 64));
-            m_all[hb] = fmaxf(m_all[hb], __shfl_xor(m_all[hb], 32, 64));
-        }
+        m_all = fmaxf(m_all, __shfl_xor(m_all, 32, 64));  // per-lane maxima -> max of the head
         if (__any(over) && lane == 0) atomicOr(&s_redo, 1);
         __syncthreads();
         if (s_redo == 0) break;
     }
 
-    // ---- finish: exp-sums per head, then per O row
+    // ---- finish: exp-sum of the lane's head (both halves), then per O row
     const int h0 = 32 * wave;
-    float lo[2][4], l_tot[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        float lt = l_part[hb] + __shfl_xor(l_part[hb], 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
-        l_tot[hb] = lt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo[hb][i] = __shfl(lt, 4 * g + i, 64);
-    }
+    const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (PARTIAL) {
         // this split's (max, exp-sum) per head; its O rows go out normalised
         const size_t pbase = (row * nsplit + split) * H;
-        if (g == 0)
+        if (hh == 0) {
+            part_ml[(pbase + h0 + hl) * 2 + 0] = m_ref;
+            part_ml[(pbase + h0 + hl) * 2 + 1] = l_tot;
+        }
+    } else if (lse != nullptr && hh == 0) {
+        lse[row * H + h0 + hl] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -__builtin_inff();
+    }
+    // O register i of column block nb holds head 8(i/4) + 4hh + i%4, column
+    // 32nb + hl: the exp-sums of those heads come from the lanes that own them
+    float inv[16];
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                part_ml[(pbase + h0 + 16 * hb + m) * 2 + 0] = m_ref[hb];
-                part_ml[(pbase + h0 + 16 * hb + m) * 2 + 1] = l_tot[hb];
-            }
-    } else if (lse != nullptr && g == 0) {
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-            lse[row * H + h0 + 16 * hb + m] =
-                l_tot[hb] > 0.f ? (m_ref[hb] + log2f(l_tot[hb])) * kLn2 : -__builtin_inff();
+    for (int i = 0; i < 16; ++i) {
+        const float li = __shfl(l_tot, 8 * (i >> 2) + 4 * hh + (i & 3), 64);
+        inv[i] = li > 0.f ? 1.f / li : 0.f;
     }
     // normalise, stage the wave's 32 x 512 bf16 block (32 KiB) in its own ring
     // stage and store it with 16-byte writes
     __syncthreads();
-    uint8_t* stage = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    uint16_t* ob = reinterpret_cast<uint16_t*>(stage);
+    uint16_t* ob = reinterpret_cast<uint16_t*>(ring + wave * STAGE);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        float inv[4];
+    for (int nb = 0; nb < DV / 32; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) inv[i] = lo[hb][i] > 0.f ? 1.f / lo[hb][i] : 0.f;
-#pragma unroll
-        for (int nv = 0; nv < DV / 16; ++nv)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ob[(16 * hb + 4 * g + i) * DV + 16 * nv + m] =
-                    __builtin_bit_cast(uint16_t, (__bf16)(o[hb][nv][i] * inv[i]));
-    }
+        for (int i = 0; i < 16; ++i)
+            ob[(8 * (i >> 2) + 4 * hh + (i & 3)) * DV + 32 * nb + hl] =
+                __builtin_bit_cast(uint16_t, (__bf16)(o[nb][i] * inv[i]));
     __syncthreads();
     uint16_t* dst = PARTIAL ? part_o + ((row * nsplit + split) * H + h0) * DV : out + (row * H + h0) * DV;
 #pragma unroll
@@ -572,9 +653,17 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kk = static_cast<const uint16_t*>(kv);
     auto* oo = static_cast<uint16_t*>(out);
+    // (a negative softmax scale takes the kernel copy that tracks max(-s))
+    const bool neg = scale_log2 < 0.f;
     if (s <= 1) {
-        sparse_mla_attn_bf16<false><<<dim3((unsigned)rows), NTA, 0, stream>>>(
-            qq, kk, idx, oo, lse, nullptr, nullptr, T, N, k, 1, k, scale_log2);
+        if (neg)
+            DSA_TIMED("sparse_mla_attn_bf16<false, true>", stream,
+                      sparse_mla_attn_bf16<false, true><<<dim3((unsigned)rows), NTA, 0, stream>>>(
+                          qq, kk, idx, oo, lse, nullptr, nullptr, T, N, k, 1, k, scale_log2));
+        else
+            DSA_TIMED("sparse_mla_attn_bf16<false, false>", stream,
+                      sparse_mla_attn_bf16<false, false><<<dim3((unsigned)rows), NTA, 0, stream>>>(
+                          qq, kk, idx, oo, lse, nullptr, nullptr, T, N, k, 1, k, scale_log2));
         return launch_status();
     }
     const int per = ((k + s - 1) / s + TK - 1) / TK * TK;
@@ -582,12 +671,19 @@ dsa_status launch_attn_bf16(const void* q, const void* kv, const int32_t* idx, v
     uint16_t* part_o = static_cast<uint16_t*>(workspace);
     float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                               align_up((size_t)rows * s * H * DV * sizeof(uint16_t)));
-    sparse_mla_attn_bf16<true><<<dim3((unsigned)(rows * s_eff)), NTA, 0, stream>>>(
-        qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, s_eff, per, scale_log2);
+    if (neg)
+        DSA_TIMED("sparse_mla_attn_bf16<true, true>", stream,
+                  sparse_mla_attn_bf16<true, true><<<dim3((unsigned)(rows * s_eff)), NTA, 0, stream>>>(
+                      qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, s_eff, per, scale_log2));
+    else
+        DSA_TIMED("sparse_mla_attn_bf16<true, false>", stream,
+                  sparse_mla_attn_bf16<true, false><<<dim3((unsigned)(rows * s_eff)), NTA, 0, stream>>>(
+                      qq, kk, idx, oo, lse, part_o, part_ml, T, N, k, s_eff, per, scale_log2));
     dsa_status st = launch_status();
     if (st != DSA_OK) return st;
-    attn_combine<<<dim3((unsigned)rows * (H / 4)), 512, 0, stream>>>(part_o, part_ml, oo, lse, s_eff,
-                                                                    (int)rows);
+    DSA_TIMED("attn_combine", stream,
+              attn_combine<<<dim3((unsigned)rows * (H / 4)), 512, 0, stream>>>(part_o, part_ml, oo,
+                                                                              lse, s_eff, (int)rows));
     return launch_status();
 }
 
@@ -596,8 +692,9 @@ dsa_status launch_attn_f32(const float* q, const float* kv, const int32_t* idx, 
                            float sm_scale, hipStream_t stream) {
     if (k > SLOTS || d_qk > 256 || Hn > 32) return DSA_ERR_UNSUPPORTED;
     if (B > 65535) return DSA_ERR_UNSUPPORTED;
-    sparse_attn_f32<<<dim3(T, B), NTF, 0, stream>>>(q, kv, idx, out, lse, T, N, Hn, d_qk, d_v, k,
-                                                    sm_scale);
+    DSA_TIMED("sparse_attn_f32", stream,
+              sparse_attn_f32<<<dim3(T, B), NTF, 0, stream>>>(q, kv, idx, out, lse, T, N, Hn, d_qk,
+                                                              d_v, k, sm_scale));
     return launch_status();
 }
 

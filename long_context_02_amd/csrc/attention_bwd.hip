@@ -731,26 +731,37 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
     const unsigned nchunks = (unsigned)((nkeys + SCAN_CHUNK - 1) / SCAN_CHUNK);
 
     const size_t n4 = (size_t)nkeys * DQK / 4;
-    zero_f32<<<dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 8192)), 256, 0, stream>>>(
-        reinterpret_cast<float4*>(dkv), n4);
+    DSA_TIMED("zero_f32", stream,
+              zero_f32<<<dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 8192)), 256, 0, stream>>>(
+                  reinterpret_cast<float4*>(dkv), n4));
     dsa_status st = launch_status();
     if (st != DSA_OK) return st;
     for (long long r0 = 0; r0 < rows; r0 += rb) {
         const int nr = (int)std::min<long long>(rb, rows - r0);
         const long long npairs = (long long)nr * k_pad;
         const unsigned gp = (unsigned)((npairs + 255) / 256);
-        zero_i32<<<dim3((unsigned)std::min<long long>((nkeys + 255) / 256, 8192)), 256, 0, stream>>>(
-            cnt, (size_t)nkeys);
-        sparse_mla_bwd_dq<<<dim3((unsigned)((nr + 7) / 8 * 16)), NT, 0, stream>>>(
-            qq, kk, idx, oo, lse, dd, dq, ws_p, ws_ds, r0, nr, T, N, k, ntile, sm_scale * kLog2e, sm_scale);
-        sparse_mla_bwd_dkv<<<dim3((unsigned)nr), NT, 0, stream>>>(qq, dd, idx, ws_p, ws_ds, contrib, r0, nr,
-                                                                  T, N, k, ntile);
-        bwd_count<<<dim3(gp), 256, 0, stream>>>(idx, cnt, rank, r0, nr, T, N, k, k_pad);
-        scan_chunk_sums<<<dim3(nchunks), 256, 0, stream>>>(cnt, sums, nkeys);
-        scan_sums<<<dim3(1), 256, 0, stream>>>(sums, (int)nchunks);
-        scan_apply<<<dim3(nchunks), 256, 0, stream>>>(cnt, sums, off, nkeys);
-        bwd_place<<<dim3(gp), 256, 0, stream>>>(idx, off, rank, list, r0, nr, T, N, k, k_pad);
-        bwd_reduce<<<dim3((unsigned)((nkeys + 3) / 4)), 256, 0, stream>>>(contrib, cnt, off, list, dkv, nkeys);
+        DSA_TIMED("zero_i32", stream,
+                  zero_i32<<<dim3((unsigned)std::min<long long>((nkeys + 255) / 256, 8192)), 256, 0,
+                             stream>>>(cnt, (size_t)nkeys));
+        DSA_TIMED("sparse_mla_bwd_dq", stream,
+                  sparse_mla_bwd_dq<<<dim3((unsigned)((nr + 7) / 8 * 16)), NT, 0, stream>>>(
+                      qq, kk, idx, oo, lse, dd, dq, ws_p, ws_ds, r0, nr, T, N, k, ntile,
+                      sm_scale * kLog2e, sm_scale));
+        DSA_TIMED("sparse_mla_bwd_dkv", stream,
+                  sparse_mla_bwd_dkv<<<dim3((unsigned)nr), NT, 0, stream>>>(
+                      qq, dd, idx, ws_p, ws_ds, contrib, r0, nr, T, N, k, ntile));
+        DSA_TIMED("bwd_count", stream,
+                  bwd_count<<<dim3(gp), 256, 0, stream>>>(idx, cnt, rank, r0, nr, T, N, k, k_pad));
+        DSA_TIMED("scan_chunk_sums", stream,
+                  scan_chunk_sums<<<dim3(nchunks), 256, 0, stream>>>(cnt, sums, nkeys));
+        DSA_TIMED("scan_sums", stream, scan_sums<<<dim3(1), 256, 0, stream>>>(sums, (int)nchunks));
+        DSA_TIMED("scan_apply", stream,
+                  scan_apply<<<dim3(nchunks), 256, 0, stream>>>(cnt, sums, off, nkeys));
+        DSA_TIMED("bwd_place", stream,
+                  bwd_place<<<dim3(gp), 256, 0, stream>>>(idx, off, rank, list, r0, nr, T, N, k, k_pad));
+        DSA_TIMED("bwd_reduce", stream,
+                  bwd_reduce<<<dim3((unsigned)((nkeys + 3) / 4)), 256, 0, stream>>>(contrib, cnt, off,
+                                                                                    list, dkv, nkeys));
         st = launch_status();
         if (st != DSA_OK) return st;
     }

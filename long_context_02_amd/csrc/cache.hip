@@ -77,13 +77,15 @@ dsa_status launch_cache_append(const float* k_new, const void* kv_new, void* k_c
                                int kv_row_bytes, bool fp8, hipStream_t stream) {
     const long long rows = (long long)B * T;
     const unsigned grid = (unsigned)((rows + CT / 64 - 1) / (CT / 64));
-    auto args = [&](auto kern) {
-        kern<<<grid, CT, 0, stream>>>(k_new, static_cast<const uint8_t*>(kv_new),
-                                      static_cast<uint8_t*>(k_cache), k_scale,
-                                      static_cast<uint8_t*>(kv_cache), pos, B, T, N, d_i, kv_row_bytes);
+    auto args = [&](auto kern, const char* name) {
+        DSA_TIMED(name, stream,
+                  kern<<<grid, CT, 0, stream>>>(k_new, static_cast<const uint8_t*>(kv_new),
+                                                static_cast<uint8_t*>(k_cache), k_scale,
+                                                static_cast<uint8_t*>(kv_cache), pos, B, T, N, d_i,
+                                                kv_row_bytes));
     };
-    if (fp8) args(cache_append_kernel<true>);
-    else args(cache_append_kernel<false>);
+    if (fp8) args(cache_append_kernel<true>, "cache_append_kernel<true>");
+    else args(cache_append_kernel<false>, "cache_append_kernel<false>");
     return launch_status();
 }
 

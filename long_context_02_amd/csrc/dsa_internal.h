@@ -92,6 +92,15 @@ dsa_status launch_attn_f32(const float* q, const float* kv, const int32_t* idx, 
                            float* lse, int B, int T, int N, int H, int d_qk, int d_v, int k,
                            float sm_scale, hipStream_t stream);
 
+// ---- sparse attention in MHA mode (attention_mha.hip) ------------------------
+// bf16 only: H = 128, latent 512 + rope 64, per-head key 128 + 64, value 128.
+// The workspace holds the up-projected per-head keys [B,N,H,192] and values
+// [B,N,H,128] (bf16) of every latent row.
+size_t attn_mha_workspace_bytes(int B, int N);
+dsa_status launch_attn_mha_bf16(const void* q, const void* kv, const void* w_uk, const void* w_uv,
+                                const int32_t* idx, void* out, float* lse, int B, int T, int N,
+                                int k, float sm_scale, void* workspace, hipStream_t stream);
+
 // ---- sparse attention backward (attention_bwd.hip) --------------------------
 // bf16 only (H = 128, d_qk = 576, d_v = 512).  dq [B,T,H,576] and dkv
 // [B,N,576] are fp32 and fully overwritten; the workspace holds one block of
@@ -124,6 +133,29 @@ dsa_status launch_indexer_kl(const float* scores, const float* p, const int32_t*
 bool validation_enabled();
 dsa_status validate_indices(const int32_t* idx, size_t n, int N, hipStream_t s);
 dsa_status validate_positions(const int32_t* pos, int B, int T, int N, hipStream_t s);
+
+// ---- per-kernel timing (profile.hip) -----------------------------------------
+// While dsa_profile_start's window is open, a Scope records a HIP event on
+// its stream when constructed and another when destroyed; DSA_TIMED wraps one
+// kernel launch in such a scope.  Names are static strings.
+namespace prof {
+bool enabled();
+class Scope {
+  public:
+    Scope(const char* name, hipStream_t s);
+    ~Scope();
+  private:
+    int slot_;
+    hipStream_t stream_;
+};
+dsa_status open_window(int max_launches);
+int close_window(dsa_kernel_time* out, int max_out, int* dropped);
+}  // namespace prof
+#define DSA_TIMED(name, stream, ...)                       \
+    do {                                                  \
+        ::dsa::prof::Scope dsa_timed_scope_(name, stream); \
+        __VA_ARGS__;                                      \
+    } while (0)
 
 inline dsa_status launch_status() {
     return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP;

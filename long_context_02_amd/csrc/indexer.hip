@@ -473,9 +473,13 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
         kpw = (kpw + TILE - 1) / TILE * TILE;
         dim3 grid(nqb, ceil_div(n_vis, kpw), B);
         if (fill_masked)
-            indexer_fp8_tiled<true><<<grid, NTT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+            DSA_TIMED("indexer_fp8_tiled<true>", stream,
+                      indexer_fp8_tiled<true><<<grid, NTT, 0, stream>>>(q, qs, k, ks, w, scores, T, N,
+                                                                        q_offset, (int)kpw));
         else
-            indexer_fp8_tiled<false><<<grid, NTT, 0, stream>>>(q, qs, k, ks, w, scores, T, N, q_offset, (int)kpw);
+            DSA_TIMED("indexer_fp8_tiled<false>", stream,
+                      indexer_fp8_tiled<false><<<grid, NTT, 0, stream>>>(q, qs, k, ks, w, scores, T, N,
+                                                                         q_offset, (int)kpw));
         return launch_status();
     }
     const int np = T <= 2 ? 1 : 2;
@@ -484,13 +488,17 @@ dsa_status launch_indexer_fp8(const uint8_t* q, const float* qs, const uint8_t* 
     kpw = std::max<long long>(1024, std::min<long long>(16384, kpw));
     kpw = (kpw + 64 * SU - 1) / (64 * SU) * (64 * SU);
     dim3 grid(ceil_div(n_vis, kpw), nqg, B);
-    auto go = [&](auto kern) {
-        kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, nullptr, T, N, q_offset, (int)kpw, 0);
+    auto go = [&](auto kern, const char* name) {
+        DSA_TIMED(name, stream,
+                  kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, scores, nullptr, T, N, q_offset,
+                                                (int)kpw, 0));
     };
     if (np == 1) {
-        if (fill_masked) go(indexer_fp8_stream<true, 1, false>); else go(indexer_fp8_stream<false, 1, false>);
+        if (fill_masked) go(indexer_fp8_stream<true, 1, false>, "indexer_fp8_stream<true, 1, false>");
+        else go(indexer_fp8_stream<false, 1, false>, "indexer_fp8_stream<false, 1, false>");
     } else {
-        if (fill_masked) go(indexer_fp8_stream<true, 2, false>); else go(indexer_fp8_stream<false, 2, false>);
+        if (fill_masked) go(indexer_fp8_stream<true, 2, false>, "indexer_fp8_stream<true, 2, false>");
+        else go(indexer_fp8_stream<false, 2, false>, "indexer_fp8_stream<false, 2, false>");
     }
     return launch_status();
 }
@@ -502,8 +510,9 @@ dsa_status launch_indexer_sample_threshold(const uint8_t* q, const float* qs, co
                                            int B, int T, int N, int q_offset, int top_k,
                                            hipStream_t stream) {
     if (!indexer_filters(B, T)) return DSA_ERR_UNSUPPORTED;
-    indexer_sample_threshold<<<dim3((unsigned)(B * T)), SMT, 0, stream>>>(q, qs, k, ks, w, seg_ws, T, N,
-                                                                        q_offset, top_k);
+    DSA_TIMED("indexer_sample_threshold", stream,
+              indexer_sample_threshold<<<dim3((unsigned)(B * T)), SMT, 0, stream>>>(
+                  q, qs, k, ks, w, seg_ws, T, N, q_offset, top_k));
     return launch_status();
 }
 
@@ -517,11 +526,13 @@ dsa_status launch_indexer_fp8_filtered(const uint8_t* q, const float* qs, const 
     const int nqg = ceil_div(T, 2 * np);
     static_assert(FKPW % (64 * SU) == 0, "filtered key ranges are whole blocks");
     dim3 grid(ceil_div(n_vis, FKPW), nqg, B);
-    auto go = [&](auto kern) {
-        kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, nullptr, seg_ws, T, N, q_offset, FKPW, top_k);
+    auto go = [&](auto kern, const char* name) {
+        DSA_TIMED(name, stream,
+                  kern<<<grid, NT, 0, stream>>>(q, qs, k, ks, w, nullptr, seg_ws, T, N, q_offset, FKPW,
+                                                top_k));
     };
-    if (np == 1) go(indexer_fp8_stream<false, 1, true>);
-    else go(indexer_fp8_stream<false, 2, true>);
+    if (np == 1) go(indexer_fp8_stream<false, 1, true>, "indexer_fp8_stream<false, 1, true>");
+    else go(indexer_fp8_stream<false, 2, true>, "indexer_fp8_stream<false, 2, true>");
     return launch_status();
 }
 
@@ -530,8 +541,9 @@ dsa_status launch_indexer_f32(const float* q, const float* k, const float* w, fl
                               bool fill_masked, hipStream_t stream) {
     if (H_I * d_I > F32_MAX_HD || H_I > 16) return DSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(N, NT), T, B);
-    indexer_f32_kernel<<<grid, NT, 0, stream>>>(q, k, w, scores, T, N, H_I, d_I, q_offset,
-                                                fill_masked ? 1 : 0);
+    DSA_TIMED("indexer_f32_kernel", stream,
+              indexer_f32_kernel<<<grid, NT, 0, stream>>>(q, k, w, scores, T, N, H_I, d_I, q_offset,
+                                                          fill_masked ? 1 : 0));
     return launch_status();
 }
 

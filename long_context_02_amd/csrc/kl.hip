@@ -210,9 +210,11 @@ dsa_status launch_indexer_kl(const float* scores, const float* p, const int32_t*
                              float* grad, int B, int T, int N, int k, int q_offset, hipStream_t stream) {
     const unsigned rows = (unsigned)((long long)B * T);
     if (idx == nullptr)
-        indexer_kl_dense<<<rows, KT, 0, stream>>>(scores, p, loss, grad, T, N, q_offset);
+        DSA_TIMED("indexer_kl_dense", stream,
+                  indexer_kl_dense<<<rows, KT, 0, stream>>>(scores, p, loss, grad, T, N, q_offset));
     else
-        indexer_kl_sparse<<<rows, ST, 0, stream>>>(scores, p, idx, loss, grad, N, k);
+        DSA_TIMED("indexer_kl_sparse", stream,
+                  indexer_kl_sparse<<<rows, ST, 0, stream>>>(scores, p, idx, loss, grad, N, k));
     return launch_status();
 }
 

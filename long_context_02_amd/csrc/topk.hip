@@ -446,17 +446,24 @@ dsa_status launch_topk(const float* scores, int32_t* idx, int B, int T, int N, i
     if (B > 65535) return DSA_ERR_UNSUPPORTED;
     const long long rows = (long long)B * T;
     if (!topk_segmented(rows)) {
-        topk_rows<<<dim3(T, B), TT, 0, stream>>>(scores, idx, T, N, k, q_offset);
+        DSA_TIMED("topk_rows", stream,
+                  topk_rows<<<dim3(T, B), TT, 0, stream>>>(scores, idx, T, N, k, q_offset));
         return launch_status();
     }
     // few long rows: several workgroups per row
     uint32_t* ws = static_cast<uint32_t*>(workspace);
     const long long n_max = std::min<long long>(N, (long long)q_offset + T);
     const int nseg = (int)((n_max + SEG - 1) / SEG);
-    topk_seg_zero<<<dim3((unsigned)rows), STT, 0, stream>>>(ws);
-    topk_seg_hist<<<dim3(nseg, (unsigned)rows), STT, 0, stream>>>(scores, ws, T, N, k, q_offset);
-    topk_seg_collect<<<dim3(nseg, (unsigned)rows), STT, 0, stream>>>(scores, ws, T, N, k, q_offset);
-    topk_seg_finalize<<<dim3((unsigned)rows), TT, 0, stream>>>(scores, ws, idx, T, N, k, q_offset);
+    DSA_TIMED("topk_seg_zero", stream, topk_seg_zero<<<dim3((unsigned)rows), STT, 0, stream>>>(ws));
+    DSA_TIMED("topk_seg_hist", stream,
+              topk_seg_hist<<<dim3(nseg, (unsigned)rows), STT, 0, stream>>>(scores, ws, T, N, k,
+                                                                            q_offset));
+    DSA_TIMED("topk_seg_collect", stream,
+              topk_seg_collect<<<dim3(nseg, (unsigned)rows), STT, 0, stream>>>(scores, ws, T, N, k,
+                                                                               q_offset));
+    DSA_TIMED("topk_seg_finalize", stream,
+              topk_seg_finalize<<<dim3((unsigned)rows), TT, 0, stream>>>(scores, ws, idx, T, N, k,
+                                                                        q_offset));
     return launch_status();
 }
 
@@ -465,8 +472,10 @@ dsa_status launch_topk_from_candidates(const uint8_t* q, const float* qs, const 
                                        int32_t* idx, int B, int T, int N, int top_k, int q_offset,
                                        void* workspace, hipStream_t stream) {
     if (top_k > KMAX || !topk_segmented((long long)B * T)) return DSA_ERR_UNSUPPORTED;
-    topk_cand_select<<<dim3((unsigned)(B * T)), TT, 0, stream>>>(
-        q, qs, kk, ks, w, scores, static_cast<const uint32_t*>(workspace), idx, T, N, top_k, q_offset);
+    DSA_TIMED("topk_cand_select", stream,
+              topk_cand_select<<<dim3((unsigned)(B * T)), TT, 0, stream>>>(
+                  q, qs, kk, ks, w, scores, static_cast<const uint32_t*>(workspace), idx, T, N, top_k,
+                  q_offset));
     return launch_status();
 }
 

@@ -240,10 +240,13 @@ def mha_keys_values(kv, w_uk, w_uv, d_c):
     w_uv = np.asarray(w_uv, dtype=np.float64)
     N = C.shape[0]
     H = w_uk.shape[0]
-    K_nope = np.einsum("hdc,nc->nhd", w_uk, C[:, :d_c])           # W_UK[h] c_s[:d_c]
-    K_rope = np.broadcast_to(C[:, None, d_c:], (N, H, C.shape[1] - d_c))
-    K = np.concatenate([K_nope, K_rope], axis=2)
-    V = np.einsum("hdc,nc->nhd", w_uv, C[:, :d_c])                # W_UV[h] c_s[:d_c]
+    d_n, d_vh = w_uk.shape[1], w_uv.shape[1]
+    K = np.empty((N, H, d_n + C.shape[1] - d_c))
+    V = np.empty((N, H, d_vh))
+    for h in range(H):
+        K[:, h, :d_n] = C[:, :d_c] @ w_uk[h].T   # W_UK[h] c_s[:d_c] for every s
+        K[:, h, d_n:] = C[:, d_c:]               # the shared rope part
+        V[:, h] = C[:, :d_c] @ w_uv[h].T         # W_UV[h] c_s[:d_c]
     return K, V
 
 

@@ -234,3 +234,26 @@ def test_forward_noalloc_rejects_before_launching():
     assert call(T=8192, N=8192, k=2048, q_offset=0) == 2
     # decode of 64 sequences at 131072 tokens fits
     assert dsa.workspace_size(dsa.OP_FORWARD, 64, 1, 131072, 8, 128, 512, 2048) <= (128 << 20)
+
+
+def test_attention_mha_rejects_bad_arguments():
+    f = dsa.lib().dsa_sparse_mla_attn_mha
+    need = dsa.workspace_size(dsa.OP_ATTN_MHA, 1, 4, 10, 8, 128, 128, 64)
+    assert need >= 10 * 128 * (192 + 128) * 2
+    with pytest.raises(ValueError):
+        dsa.workspace_size(dsa.OP_ATTN_MHA, 1, 4, 10, 8, 64, 128, 64)
+
+    def call(H=128, dc=512, dr=64, dn=128, dvh=128, k=64, scale=0.07, dt=dsa.BF16, ws=P, wsb=None,
+             ptrs=None):
+        ptrs = ptrs or [P, P, P, P, P, P, None]
+        return f(*ptrs, 1, 4, 10, H, dc, dr, dn, dvh, k, scale, dt, ws, need if wsb is None else wsb,
+                 None)
+
+    assert call(ptrs=[P, P, None, P, P, P, None]) == 1      # no W_UK
+    assert call(ptrs=[P, P, P, P, P, ctypes.c_void_p(0x10002), None]) == 1  # misaligned out
+    assert call(H=64) == 2 and call(dc=256) == 2 and call(dr=32) == 2
+    assert call(dn=64) == 2 and call(dvh=64) == 2
+    assert call(k=0) == 1 and call(k=2049) == 2
+    assert call(scale=float("nan")) == 1
+    assert call(dt=dsa.F32) == 2 and call(dt=7) == 1
+    assert call(ws=None) == 3 and call(wsb=need - 1) == 3

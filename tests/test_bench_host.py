@@ -5,6 +5,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -59,17 +60,59 @@ def test_roofline_picks_the_binding_roof():
     assert bench.phase_floor(wd) == pytest.approx(wd["bytes"] / 8000e9)
 
 
-def test_traffic_summary_is_ignored_after_a_source_change(monkeypatch):
+def test_traffic_summary_is_ignored_after_a_source_change(monkeypatch, tmp_path):
     wl = WORKLOADS["decode_128k"]
-    path = os.path.join(ROOT, "profiles", "attention_decode_128k_traffic.txt")
-    if not os.path.exists(path):
-        pytest.skip("no attention traffic summary committed")
-    real = bench.source_hash("attention")
-    with open(path) as f:
-        recorded = [ln.split("=", 1)[1].strip() for ln in f if ln.startswith("kernel_source_sha256")]
-    if recorded != [real]:
-        assert bench.measured_traffic("attention", wl) is None
-    else:
-        assert bench.measured_traffic("attention", wl) > 0
-    monkeypatch.setattr(bench, "source_hash", lambda phase: "0" * 64)
-    assert bench.measured_traffic("attention", wl) is None
+    kernel = "sparse_mla_attn_bf16<true>"
+    assert bench.profile_name(kernel) == "sparse_mla_attn_bf16_true"
+    real = bench.source_hash(kernel)
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "sparse_mla_attn_bf16_true_decode_128k_traffic.txt").write_text(
+        f"# test summary\nhbm_bytes_per_launch = 123456\nkernel_source_sha256 = {real}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_hash", lambda k: real)
+    assert bench.measured_traffic(kernel, wl) == 123456
+    monkeypatch.setattr(bench, "source_hash", lambda k: "0" * 64)
+    assert bench.measured_traffic(kernel, wl) is None
+
+
+def test_kernel_work_attribution():
+    w = bench.work(WORKLOADS["decode_128k"])
+    assert bench.kernel_work("indexer_fp8_stream<false, 1, true>", w) is w["indexer"]
+    assert bench.kernel_work("sparse_mla_attn_bf16<true>", w) is w["attention"]
+    assert bench.kernel_work("indexer_fp8_tiled<false>", w) is w["indexer"]
+    assert bench.kernel_work("topk_rows", w) is w["topk"]
+    assert bench.kernel_work("attn_combine", w) is None
+    assert bench.kernel_work("indexer_sample_threshold", w) is None
+
+
+def test_roofline_against_measured_peaks():
+    w = bench.work(WORKLOADS["decode_128k"])["attention"]
+    r = bench.roofline("a", w, 5e-5, {"hbm_read_gbs": 6000.0})
+    assert r["bound"] == "hbm"
+    assert r["frac_of_measured"] == pytest.approx(r["achieved"] / 6000.0, rel=1e-3)
+    wc = bench.work(WORKLOADS["chunk_128k"])["indexer"]
+    rc = bench.roofline("i", wc, 5e-4, {"fp8_mfma_tflops": 3000.0})
+    assert rc["bound"] == "mfma" and rc["peak"] == 5000.0
+    assert rc["frac_of_measured"] == pytest.approx(rc["achieved"] / 3000.0, rel=1e-3)
+
+
+def test_cpu_info_reports_affinity_cores():
+    model, cores, threads = bench.cpu_info()
+    assert cores == len(os.sched_getaffinity(0))
+    assert isinstance(model, str) and model
+    assert threads >= 1
+
+
+def test_row_parity_rule():
+    wl = WORKLOADS["decode_128k"].with_(k=4)
+    scores = np.array([5.0, 1.0, 4.0, 3.0, 2.0, 4.0005, 0.5])
+    ref_sel = np.array([0, 2, 3, 5])
+    out = np.zeros((2, 3))
+    assert bench._check_row(np.array([0, 2, 3, 5]), out, scores, ref_sel, out, wl, 7, "x") is None
+    # token 2 (4.0) and 5 (4.0005) are not at the k-th score (3.0): a swap
+    # with token 4 (2.0) is outside the band
+    assert "band" in bench._check_row(np.array([0, 2, 4, 5]), out, scores, ref_sel, out, wl, 7, "x")
+    assert "malformed" in bench._check_row(np.array([0, 3, 2, 5]), out, scores, ref_sel, out, wl, 7, "x")
+    assert "attention" in bench._check_row(np.array([0, 2, 3, 5]), out + 0.05, scores, ref_sel, out, wl,
+                                           7, "x")
