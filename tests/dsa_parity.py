@@ -136,3 +136,46 @@ def sample_rows(T, k, rng, extra=6):
             rows.add(t)
     rows.update(int(x) for x in rng.integers(0, T, extra))
     return sorted(rows)
+
+
+# ---- poisoned outputs and guarded buffers --------------------------------
+GUARD_BYTES = 4096  # canary bytes before and after every guarded buffer
+_CANARY = {1: (torch.uint8, 0x5A), 2: (torch.int16, 0x5A5A), 4: (torch.int32, 0x5A5A5A5A)}
+
+
+class Guarded:
+    """A device buffer of `shape` with canary bytes on both sides, its own
+    elements poisoned with `fill` (NaN for floats: any element the call
+    fails to write stays visible).  check() asserts that no canary byte
+    changed.  Alignment: the buffer starts GUARD_BYTES into a fresh
+    allocation, so it keeps the allocation's 256-byte alignment."""
+
+    def __init__(self, shape, dtype, dev, fill):
+        size = torch.tensor([], dtype=dtype).element_size()
+        n = int(np.prod(shape))
+        g = GUARD_BYTES // size
+        self.full = torch.empty(n + 2 * g, dtype=dtype, device=dev)
+        bits_dtype, canary = _CANARY[size]
+        self.bits = self.full.view(bits_dtype)
+        self.bits.fill_(canary)
+        self.canary = canary
+        self.g = g
+        self.n = n
+        self.view = self.full[g:g + n].view(shape)
+        if n:
+            if isinstance(fill, int) and dtype.is_floating_point:
+                self.view.view(bits_dtype).fill_(fill)
+            else:
+                self.view.fill_(fill)
+
+    def check(self, where=""):
+        lo = self.bits[:self.g]
+        hi = self.bits[self.g + self.n:]
+        ok = bool((lo == self.canary).all()) and bool((hi == self.canary).all())
+        assert ok, f"{where}: a write landed outside the buffer (canary changed)"
+
+
+def poisoned_workspace(nbytes, dev):
+    """A workspace whose bytes all start as 0xA5 (a NaN-free but absurd
+    pattern for counters and keys), guarded on both sides."""
+    return Guarded((max(int(nbytes), 1),), torch.uint8, dev, 0xA5)

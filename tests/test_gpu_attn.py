@@ -5,7 +5,7 @@ import torch
 
 import long_context_02_amd as dsa
 import oracle
-from dsa_parity import check_attention, check_lse, gpu_device, np64
+from dsa_parity import Guarded, check_attention, check_lse, gpu_device, np64, poisoned_workspace
 from long_context_02_amd.synth import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,8 +30,17 @@ def _run(wl, idx_np, seed, where):
     inp = make_inputs(wl, seed=seed, device="cpu")
     q, kv = inp["q"].to(dev), inp["kv"].to(dev)
     print(f"[attn] {where}", flush=True)
-    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx_np).to(dev), wl.d_v, wl.sm_scale)
+    B, T, H = q.shape[:3]
+    k = idx_np.shape[-1]
+    out_g = Guarded((B, T, H, wl.d_v), q.dtype, dev, float("nan"))
+    lse_g = Guarded((B, T, H), torch.float32, dev, float("nan"))
+    need = dsa.workspace_size(dsa.OP_ATTN, B, T, wl.N, 1, H, wl.d_v, k) if 1 <= k <= 2048 else 0
+    ws = poisoned_workspace(need, dev)
+    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx_np).to(dev), wl.d_v, wl.sm_scale,
+                                   out=out_g.view, lse=lse_g.view, workspace=ws.view)
     torch.cuda.synchronize()
+    for name, buf in (("out", out_g), ("lse", lse_g), ("workspace", ws)):
+        buf.check(f"{where} {name}")
     ref_o, ref_l = oracle.sparse_mqa_attention(np64(inp["q"]), np64(inp["kv"]), idx_np, wl.d_v,
                                                wl.sm_scale)
     bf16 = wl.dtype == "bf16"

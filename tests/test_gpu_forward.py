@@ -2,8 +2,10 @@
 
 Small shapes are checked row by row in full; the full-size workloads run
 whole on the GPU (the launch configuration the benchmark times) and are
-checked on sampled rows that the oracle recomputes one by one: the first and
-last row, the rows around t = k, and random ones.
+checked on rows that the oracle recomputes one by one: every sequence at
+decode; the first and last row, the rows around t = k and random ones at
+prefill and chunked prefill.  Outputs and the workspace start poisoned
+(NaN, -7, 0xA5 bytes) and sit between canary guards that must stay intact.
 """
 import numpy as np
 import pytest
@@ -11,18 +13,31 @@ import torch
 
 import long_context_02_amd as dsa
 import oracle
-from dsa_parity import (check_attention, check_index_set, check_lse, gpu_device, np64,
-                        sample_rows, to_device)
+from dsa_parity import (Guarded, check_attention, check_index_set, check_lse, gpu_device, np64,
+                        poisoned_workspace, sample_rows, to_device)
 from long_context_02_amd.synth import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
 
 def _forward(wl, g):
-    return dsa.forward(g["q_idx"], g["k_idx"], g["w"], g["q"], g["kv"], k=wl.k,
-                       q_offset=wl.q_offset, d_v=wl.d_v, sm_scale=wl.sm_scale,
-                       q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"],
-                       lse=True, idx_out=True)
+    """dsa_forward into NaN/-7-poisoned outputs on a poisoned workspace, all
+    with canary guards; the guards are checked after the call."""
+    B, T, N = g["q_idx"].shape[0], g["q_idx"].shape[1], g["k_idx"].shape[1]
+    dev = g["q"].device
+    out = Guarded((B, T, wl.H, wl.d_v), g["q"].dtype, dev, float("nan"))
+    lse = Guarded((B, T, wl.H), torch.float32, dev, float("nan"))
+    idx = Guarded((B, T, wl.k), torch.int32, dev, -7)
+    ws = poisoned_workspace(dsa.workspace_size(dsa.OP_FORWARD, B, T, N, wl.H_I, wl.H, wl.d_v, wl.k),
+                            dev)
+    dsa.forward(g["q_idx"], g["k_idx"], g["w"], g["q"], g["kv"], k=wl.k,
+                q_offset=wl.q_offset, d_v=wl.d_v, sm_scale=wl.sm_scale,
+                q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"],
+                out=out.view, lse=lse.view, idx_out=idx.view, workspace=ws.view)
+    torch.cuda.synchronize()
+    for name, buf in (("out", out), ("lse", lse), ("idx", idx), ("workspace", ws)):
+        buf.check(f"dsa_forward {name}")
+    return out.view, lse.view, idx.view
 
 
 def _check_rows(wl, g, out, lse, idx, rows, where):
@@ -33,9 +48,8 @@ def _check_rows(wl, g, out, lse, idx, rows, where):
     for (b, t) in rows:
         if b not in keys:
             kc = np64(g["k_idx"][b])
-            keys = {b: (oracle.dequantize(kc, np64(g["k_idx_scale"][b])) if bf16 else kc,
-                        g["kv"][b].float().cpu().numpy())}
-        K, kv_b = keys[b]
+            keys = {b: oracle.dequantize(kc, np64(g["k_idx_scale"][b])) if bf16 else kc}
+        K = keys[b]
         q_row = (oracle.dequantize(np64(g["q_idx"][b, t]), np64(g["q_idx_scale"][b, t])) if bf16
                  else np64(g["q_idx"][b, t]))
         n_cand = min(wl.N, wl.q_offset + t + 1)
@@ -43,7 +57,12 @@ def _check_rows(wl, g, out, lse, idx, rows, where):
         sel = oracle.topk_select_row(I, wl.k, n_cand)
         gi = idx[b, t].cpu().numpy()
         exact += check_index_set(gi, I, sel, wl.k, n_cand, f"{where} row ({b},{t})")
-        o_ref, l_ref = oracle.sparse_mqa_attention_row(np64(g["q"][b, t]), kv_b, gi, wl.d_v,
+        # the selected latent rows only (copied, not computed, on the device);
+        # the index set is ascending and -1 padded, so slot i reads row i
+        n = int((gi >= 0).sum())
+        kv_sel = np64(g["kv"][b, torch.as_tensor(gi[:n], dtype=torch.long, device=g["kv"].device)])
+        local = np.where(np.arange(gi.size) < n, np.arange(gi.size), -1)
+        o_ref, l_ref = oracle.sparse_mqa_attention_row(np64(g["q"][b, t]), kv_sel, local, wl.d_v,
                                                        wl.sm_scale)
         check_attention(np64(out[b, t]), o_ref, bf16, f"{where} row ({b},{t})")
         check_lse(np64(lse[b, t]), l_ref, bf16, f"{where} row ({b},{t})")
@@ -97,7 +116,7 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     rng = np.random.default_rng(42)
     if wl.T == 1:
-        rows = [(b, 0) for b in sorted({0, wl.B - 1, *rng.integers(0, wl.B, 2).tolist()})]
+        rows = [(b, 0) for b in range(wl.B)]  # decode: every sequence
     else:
         rows = [(0, t) for t in sample_rows(wl.T, wl.k, rng)]
     _check_rows(wl, g, out, lse, idx, rows, name)

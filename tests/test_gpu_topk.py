@@ -88,3 +88,34 @@ def test_negative_and_infinite_scores():
     s[0, :, ::17] = float("-inf")
     s[0, :, ::29] = float("inf")
     _check(s, 300, 4096 - 16, "signed")
+
+
+def test_one_pass_rows_nan_inf_signed_zero_ties():
+    """256 rows of 40000 candidates take the one-pass sampled-threshold path;
+    its special values: NaN (ranks lowest), -inf, +-0 (equal), heavy exact
+    ties, and rows whose sample is mostly or all NaN (threshold 0: every key
+    passes, the wave regions overflow and the row falls back)."""
+    g = _gen(13)
+    T, N = 256, 40000
+    s = torch.randn(1, T, N, generator=g)
+    s[torch.rand(1, T, N, generator=g) < 0.02] = float("nan")
+    s[torch.rand(1, T, N, generator=g) < 0.02] = float("-inf")
+    s[torch.rand(1, T, N, generator=g) < 0.02] = 0.0
+    s[torch.rand(1, T, N, generator=g) < 0.02] = -0.0
+    s[0, 5][torch.rand(N, generator=g) < 0.95] = float("nan")   # mostly NaN
+    s[0, 6] = float("nan")
+    s[0, 6, ::400] = 1.0                                         # 100 numbers, rest NaN
+    s[0, 7] = torch.randint(0, 4, (N,), generator=g).float() * 0.5  # four values
+    s[0, 8] = float("-inf")
+    s[0, 8, ::7] = torch.randn(len(range(0, N, 7)), generator=g)  # mostly -inf
+    s[0, 9] = 0.0
+    s[0, 9, ::2] = -0.0                                          # all zeros, both signs
+    # NaN at every sampled position of a row that is otherwise finite (the
+    # sample reads 16-key blocks starting at j * (n - 16) / 127)
+    n10 = N - T + 10 + 1
+    for j in range(128):
+        st = (j * (n10 - 16)) // 127
+        s[0, 10, st:st + 16] = float("nan")
+    s[0, 11] = 2.0                                               # one value everywhere
+    s[0, 11, 100:110] = float("nan")
+    _check(s, 2048, N - T, "one-pass special values")
