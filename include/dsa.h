@@ -39,8 +39,9 @@
  *    are skipped as each call describes.
  *
  * Supported shapes
- *  - indexer: (H_I, d_I, idx_dtype) = (8, 128, DSA_FP8_E4M3FN) or
- *    (1..16, 1..256, DSA_F32);
+ *  - indexer: (H_I, d_I, idx_dtype) = (8, 128, DSA_FP8_E4M3FN) with
+ *    N < 2^24 keys per sequence (32-bit byte offsets into the keys and the
+ *    score rows), or (1..16, 1..256, DSA_F32);
  *  - attention: (H, d_qk, d_v, attn_dtype) = (128, 576, 512, DSA_BF16) with
  *    N < 2^31 / 1152 latent rows per sequence (the gather addresses one
  *    sequence's rows with 32-bit byte offsets), or (1..32, 1..256, 1..d_qk,

@@ -43,6 +43,7 @@ dsa_status check_indexer(const void* q_idx, const float* q_scale, const void* k_
         if (!q_scale || !k_scale || !aligned16(q_scale) || !aligned16(k_scale))
             return DSA_ERR_INVALID_ARG;
         if (H_I != 8 || d_I != 128) return DSA_ERR_UNSUPPORTED;
+        if (N >= (1 << 24)) return DSA_ERR_UNSUPPORTED;  // 32-bit byte offsets into keys and scores
         return DSA_OK;
     }
     if (dt == DSA_F32) {

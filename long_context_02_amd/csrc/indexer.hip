@@ -30,30 +30,8 @@ namespace dsa {
 namespace {
 
 constexpr int NT = 256;    // threads per workgroup (4 waves)
-
-// Load the A fragments (one query group of 4 queries, both head halves) and
-// the per-lane head weights w * q_scale of the query whose scores this lane
-// produces.  Queries at or beyond T get zeros.
-__device__ __forceinline__ void load_queries(const uint8_t* __restrict__ q,
-                                             const float* __restrict__ qs,
-                                             const float* __restrict__ w, size_t row0,
-                                             int tq0, int T, int lane, i32x8* a, float* ws) {
-    const int m = lane & 15, kb = lane >> 4;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int t = tq0 + (m >> 2), h = 4 * hh + (m & 3);
-        if (t < T) {
-            const uint4* p = reinterpret_cast<const uint4*>(q + ((row0 + t) * HI + h) * DI + 32 * kb);
-            a[hh] = pack8(p[0], p[1]);
-        } else {
-            a[hh] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
-    const int t = tq0 + kb;
-#pragma unroll
-    for (int j = 0; j < HI; ++j)
-        ws[j] = t < T ? w[(row0 + t) * HI + j] * qs[(row0 + t) * HI + j] : 0.f;
-}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBuf = 0x00020000;  // buffer resource word 3: raw (untyped) 32-bit data
 
 __device__ void fill_neg_inf(float* __restrict__ out_b, int t0, int t1, int N, int s0, int s1) {
     const float ninf = -__builtin_inff();
@@ -70,9 +48,8 @@ constexpr int OST = 80;     // LDS floats per staged output row (64 + 16: rows 1
 constexpr int NTT = 512;    // threads of the tiled kernel: 8 waves x 8 queries
 constexpr int QPW = TQB / (NTT / 64);   // queries per wave
 constexpr int GPW = QPW / 4;            // 4-query MFMA groups per wave
-
 template <bool FILL>
-__global__ __launch_bounds__(NTT) void indexer_fp8_tiled(
+__global__ __launch_bounds__(NTT) __attribute__((amdgpu_waves_per_eu(4))) void indexer_fp8_tiled(
     const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
     int T, int N, int q_offset, int keys_per_wg) {
@@ -102,62 +79,96 @@ __global__ __launch_bounds__(NTT) void indexer_fp8_tiled(
         float ws[GPW][HI];
 #pragma unroll
         for (int g = 0; g < GPW; ++g) load_queries(q, qs, w, row0, tw0 + 4 * g, T, lane, a[g], ws[g]);
-        float* ost = lds_o[wave];
-
-        // cooperative staging: 512 16-byte chunks per tile, one per thread
+        // cooperative staging: 512 16-byte chunks per tile, one per thread,
+        // through buffer resources (the tile's key offset is a scalar; keys
+        // at or past N read as zeros)
         const int c_key = tid >> 3, c_piece = tid & 7;
-        uint4 r0;
+        // (byte counts and offsets are 32-bit: N < 2^24, checked on the host)
+        const auto k_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(k_b), 0,
+                                                            (int)((unsigned)N * DI), kRawBuf);
+        const auto ks_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ks_b), 0, 4 * N, kRawBuf);
+        const int k_voff = DI * c_key + 16 * c_piece;
+        u32x4 r0;
         float rks = 0.f;
         auto fetch = [&](int s0) {
-            const uint4 zero = {0u, 0u, 0u, 0u};
-            const int s_a = s0 + c_key;
-            r0 = s_a < N ? *reinterpret_cast<const uint4*>(k_b + (size_t)s_a * DI + 16 * c_piece) : zero;
-            if (tid < TILE) rks = (s0 + tid) < N ? ks_b[s0 + tid] : 0.f;
+            r0 = __builtin_amdgcn_raw_buffer_load_b128(k_rs, k_voff, s0 * DI, 0);
+            if (tid < TILE) rks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ks_rs, 4 * tid, 4 * s0, 0));
         };
         auto stage = [&](int buf) {
-            *reinterpret_cast<uint4*>(&lds_k[buf][c_key * ROWB + 16 * c_piece]) = r0;
+            *reinterpret_cast<u32x4*>(&lds_k[buf][c_key * ROWB + 16 * c_piece]) = r0;
             if (tid < TILE) lds_ks[buf][tid] = rks;
         };
+        // score stores through a buffer over the workgroup's rows [t0, t_end):
+        // per lane a fixed byte offset per row step, the tile's key offset a
+        // scalar; stores to rows at or past t_end fall outside and are dropped
+        const auto o_rs = __builtin_amdgcn_make_buffer_rsrc(out_b + (size_t)t0 * N, 0,
+                                                            (int)(4u * (unsigned)(t_end - t0) * (unsigned)N), kRawBuf);
+        int o_voff[QPW / 4];
+#pragma unroll
+        for (int j = 0; j < QPW / 4; ++j)
+            o_voff[j] = (int)(4u * ((unsigned)(tw0 - t0 + 4 * j + (lane >> 4)) * (unsigned)N + 4u * (lane & 15)));
 
-        fetch(s_begin);
-        stage(0);
-        __syncthreads();
-        for (int it = 0; it < n_tiles; ++it) {
+        // One tile: the scores of its 64 keys for the wave's queries into LDS,
+        // then out as whole 256-byte row segments.  MASKED applies the causal
+        // mask and the range checks; the leading tiles, whose keys every query
+        // of the workgroup sees, skip them.
+        auto tile = [&](int it, auto masked) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked)::value;
             const int s0 = s_begin + it * TILE;
             const int buf = it & 1;
             const bool more = it + 1 < n_tiles;
             if (more) fetch(s0 + TILE);
+            float* ost = lds_o[wave];
             if (tw0 < t_end) {
-                // a clean tile: every key visible to all of the wave's queries, all in range
-                const bool clean = vec_out && s0 + TILE - 1 <= q_offset + tw0 && tw0 + QPW <= T &&
-                                   s0 + TILE <= s_end;
-                // the scores of the tile into LDS; the causal mask only on the
-                // tiles that need it (two copies of the loop)
-                auto scores16 = [&](auto masked) __attribute__((always_inline)) {
-#pragma unroll
-                    for (int sub = 0; sub < TILE / 16; ++sub) {
-                        const int key = 16 * sub + m;
-                        const uint8_t* src = &lds_k[buf][key * ROWB + 32 * kb];
-                        const i32x8 bf = pack8(*reinterpret_cast<const uint4*>(src),
-                                               *reinterpret_cast<const uint4*>(src + 16));
-                        const float ksc = lds_ks[buf][key];
-                        f32x4 acc[GPW][2];
-#pragma unroll
-                        for (int g = 0; g < GPW; ++g) {
-                            acc[g][0] = mfma_fp8(a[g][0], bf);
-                            acc[g][1] = mfma_fp8(a[g][1], bf);
-                        }
-#pragma unroll
-                        for (int g = 0; g < GPW; ++g) {
-                            float sc = head_sum(acc[g][0], acc[g][1], ws[g]) * ksc;
-                            if (decltype(masked)::value && s0 + key > q_offset + tw0 + 4 * g + kb)
-                                sc = -__builtin_inff();
-                            ost[(4 * g + kb) * OST + key] = sc;
-                        }
-                    }
+                // Software pipelined over the tile's four 16-key steps and the
+                // wave's two query groups: the MFMAs of (step j + 1, group g)
+                // are issued right after the epilogue of (j, g) has read the
+                // group's accumulators, so an epilogue never waits for a
+                // product just issued and each group needs one accumulator set.
+                constexpr int NSUB = TILE / 16;
+                static_assert(GPW == 2, "two query groups per wave");
+                i32x8 bfr[2];
+                float kscr[2];
+                f32x4 acc[GPW][2];
+                auto ldb = [&](int sub) __attribute__((always_inline)) {
+                    const uint8_t* src = &lds_k[buf][(16 * sub + m) * ROWB + 32 * kb];
+                    bfr[sub & 1] = pack8(*reinterpret_cast<const uint4*>(src),
+                                         *reinterpret_cast<const uint4*>(src + 16));
+                    kscr[sub & 1] = lds_ks[buf][16 * sub + m];
                 };
-                if (clean) scores16(std::false_type{});
-                else scores16(std::true_type{});
+                auto mm = [&](int sub, int g) __attribute__((always_inline)) {
+                    acc[g][0] = mfma_fp8(a[g][0], bfr[sub & 1]);
+                    acc[g][1] = mfma_fp8(a[g][1], bfr[sub & 1]);
+                };
+                auto epi = [&](int sub, int g) __attribute__((always_inline)) {
+                    const int key = 16 * sub + m;
+                    float sc = head_sum(acc[g][0], acc[g][1], ws[g]) * kscr[sub & 1];
+                    if (MASKED && s0 + key > q_offset + tw0 + 4 * g + kb) sc = -__builtin_inff();
+                    ost[(4 * g + kb) * OST + key] = sc;
+                };
+                ldb(0);
+                mm(0, 0);
+                mm(0, 1);
+                ldb(1);
+#pragma unroll
+                for (int sub = 0; sub < NSUB; ++sub) {
+                    // (scheduling barriers keep this order: the compiler would
+                    // otherwise move each epilogue next to the MFMAs it reads
+                    // and wait for them)
+                    __builtin_amdgcn_sched_barrier(0);
+                    epi(sub, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (sub + 1 < NSUB) mm(sub + 1, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    epi(sub, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (sub + 1 < NSUB) mm(sub + 1, 1);
+                    if (sub + 2 < NSUB) ldb(sub + 2);
+                }
+                // the next tile goes into the other buffer now, before this
+                // tile's score stores are issued: waiting for its loads then
+                // does not also wait for the stores
+                if (more) stage(buf ^ 1);
                 // QPW rows x 64 keys out of LDS: lane l takes 16 bytes of row
                 // 4j + l/16 per step, each row a whole 256-byte segment
                 const int c = lane & 15;
@@ -165,25 +176,39 @@ __global__ __launch_bounds__(NTT) void indexer_fp8_tiled(
                 for (int j = 0; j < QPW / 4; ++j) {
                     const int r = 4 * j + (lane >> 4);
                     const int t = tw0 + r;
-                    const float4 v = *reinterpret_cast<const float4*>(&ost[r * OST + 4 * c]);
-                    float* dst = out_b + (size_t)t * N + s0 + 4 * c;
-                    if (clean) {
-                        *reinterpret_cast<float4*>(dst) = v;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(&ost[r * OST + 4 * c]);
+                    if (!MASKED) {
+                        __builtin_amdgcn_raw_buffer_store_b128(v, o_rs, o_voff[j], 4 * s0, 0);
                     } else if (t < T) {
                         if (vec_out) {
-                            if (s0 + 4 * c < s_end) *reinterpret_cast<float4*>(dst) = v;
+                            if (s0 + 4 * c < s_end) __builtin_amdgcn_raw_buffer_store_b128(v, o_rs, o_voff[j], 4 * s0, 0);
                         } else {
-                            const float vv[4] = {v.x, v.y, v.z, v.w};
+                            float* dst = out_b + (size_t)t * N + s0 + 4 * c;
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                if (s0 + 4 * c + e < s_end) dst[e] = vv[e];
+                                if (s0 + 4 * c + e < s_end) dst[e] = __builtin_bit_cast(float, v[e]);
                         }
                     }
                 }
+            } else if (more) {
+                stage(buf ^ 1);
             }
-            if (more) stage(buf ^ 1);
             __syncthreads();
+        };
+
+        // leading tiles with every key visible to every query of the
+        // workgroup, all inside [s_begin, s_end), full 16-byte row chunks
+        int n_clean = 0;
+        if (vec_out && t0 + TQB <= T) {
+            const int lim = min(q_offset + t0 + 1, s_end);  // keys below lim are clean
+            n_clean = lim > s_begin ? min(n_tiles, (lim - s_begin) / TILE) : 0;
         }
+        fetch(s_begin);
+        stage(0);
+        __syncthreads();
+        int it = 0;
+        for (; it < n_clean; ++it) tile(it, std::false_type{});
+        for (; it < n_tiles; ++it) tile(it, std::true_type{});
     }
     if (FILL) {
         const int f0 = s_begin + n_tiles * TILE;

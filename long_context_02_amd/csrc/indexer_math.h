@@ -46,6 +46,34 @@ __device__ __forceinline__ float head_sum(const f32x4& acc0, const f32x4& acc1, 
     return s;
 }
 
+// ---- tiled layout: the 16 MFMA rows are 4 queries x 4 heads ---------------
+// Two MFMAs (heads 0-3, then 4-7) give lane l all 8 head dots of query
+// tq0 + l/16 and key l%16; head_sum (above) in that order, then the key scale.
+
+// Load the A fragments (one query group of 4 queries, both head halves) and
+// the per-lane head weights w * q_scale of the query whose scores this lane
+// produces.  Queries at or beyond T get zeros.
+__device__ __forceinline__ void load_queries(const uint8_t* __restrict__ q,
+                                             const float* __restrict__ qs,
+                                             const float* __restrict__ w, size_t row0,
+                                             int tq0, int T, int lane, i32x8* a, float* ws) {
+    const int m = lane & 15, kb = lane >> 4;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int t = tq0 + (m >> 2), h = 4 * hh + (m & 3);
+        if (t < T) {
+            const uint4* p = reinterpret_cast<const uint4*>(q + ((row0 + t) * HI + h) * DI + 32 * kb);
+            a[hh] = pack8(p[0], p[1]);
+        } else {
+            a[hh] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    const int t = tq0 + kb;
+#pragma unroll
+    for (int j = 0; j < HI; ++j)
+        ws[j] = t < T ? w[(row0 + t) * HI + j] * qs[(row0 + t) * HI + j] : 0.f;
+}
+
 // ---- stream layout: the 16 MFMA rows are 2 queries x 8 heads -------------
 // C lane l holds rows 4*(l/16)+i: query (l/16)/2 of the pair, heads
 // 4*((l/16)&1)+i; a score's two head halves sit in lanes l and l ^ 16.

@@ -102,6 +102,7 @@ def test_indexer_rejects_bad_arguments():
     assert call(T=0) == 1
     assert call(q_offset=-1) == 1
     assert call(H_I=4) == 2 and call(d_I=64) == 2         # FP8 supports (8, 128)
+    assert call(N=1 << 24, q_offset=(1 << 24) - 4) == 2   # FP8 keys: 32-bit byte offsets
     assert call(dt=dsa.BF16) == 2
     assert call(dt=9) == 1
     assert call(dt=dsa.F32) == 1                          # f32 takes no scales
