@@ -90,6 +90,10 @@ __device__ __forceinline__ void qk_last(f32x16& d, const bf16x8& a, const bf16x8
 __device__ __forceinline__ int lat_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
+// P of one tile as the value product's A operands: 4 head blocks x 2 k steps
+// x 64 lanes x 16 bytes.
+constexpr int PBYTES = NWV * 2 * 64 * 16;
+
 template <bool PARTIAL, bool NEG>
 __global__ __launch_bounds__(NTA) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_attn_bf16(
@@ -99,10 +103,15 @@ void sparse_mla_attn_bf16(
     float scale_log2) {
     // four ring stages; tile t lives in stage t % 4
     __shared__ __attribute__((aligned(16))) uint8_t ring[4 * STAGE];
-    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS + 4 * TK];
-    __shared__ int s_last;
-    __shared__ int s_redo;
-    __shared__ unsigned s_notfull[(SLOTS + 4 * TK) / TK / 32 + 1];  // tiles with an invalid slot
+    __shared__ __attribute__((aligned(16))) int32_t sidx[SLOTS];
+    // the current tile's P, shared by the four waves; outside the tile loop
+    // the same bytes hold the workgroup's scalars (setup, pass end) and the
+    // exp-sums of all heads (finish)
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[PBYTES];
+    int* const s_last = reinterpret_cast<int*>(pbuf);
+    int* const s_redo = reinterpret_cast<int*>(pbuf) + 1;
+    unsigned* const s_notfull = reinterpret_cast<unsigned*>(pbuf) + 4;  // tiles with an invalid slot
+    float* const s_l = reinterpret_cast<float*>(pbuf);
 
     // (split batches only: causal prefill rows differ in length, and giving
     // each XCD a contiguous range of them would unbalance the XCDs)
@@ -119,8 +128,8 @@ void sparse_mla_attn_bf16(
     const uint16_t* __restrict__ kv_b = kv + (size_t)b * N * DQK;
 
     // ---- slot indices of this workgroup; the last valid one
-    if (tid == 0) s_last = -1;
-    if (tid < (SLOTS + 4 * TK) / TK / 32 + 1) s_notfull[tid] = 0;
+    if (tid == 0) *s_last = -1;
+    if (tid < SLOTS / TK / 32) s_notfull[tid] = 0;
     __syncthreads();
     int my_last = -1;
     const int nslots_pad = (nslots + TK - 1) / TK * TK;
@@ -132,7 +141,7 @@ void sparse_mla_attn_bf16(
         // waited for (a loop that stores each index as it arrives waits for
         // one memory round trip per iteration), and Q's loads right behind
         // them, so that Q arrives while the indices are used
-        constexpr int PER = (SLOTS + 4 * TK + NTA - 1) / NTA;
+        constexpr int PER = (SLOTS + NTA - 1) / NTA;
         int id[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -146,17 +155,18 @@ void sparse_mla_attn_bf16(
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = tid + j * NTA;
-            if (i < nslots_pad + 4 * TK) {
+            if (i < nslots_pad) {
                 sidx[i] = id[j];
                 if (id[j] >= 0 && id[j] < N) my_last = i;
-                else if (i < nslots_pad) atomicOr(&s_notfull[i / (32 * TK)], 1u << ((i / TK) & 31));
+                else atomicOr(&s_notfull[i / (32 * TK)], 1u << ((i / TK) & 31));
             }
         }
     }
-    if (my_last >= 0) atomicMax(&s_last, my_last);
+    if (my_last >= 0) atomicMax(s_last, my_last);
 
     __syncthreads();
-    const int last = s_last;
+    const int last = *s_last;
+    const unsigned nf0 = s_notfull[0], nf1 = s_notfull[1];  // (read before the first P is written)
     const int n_tiles = (last + TK) / TK;  // 0 when no slot is valid
     // rows of invalid slots are loaded from a selected row (their weight is 0)
     const int dummy = last >= 0 ? sidx[last] : 0;
@@ -168,10 +178,12 @@ void sparse_mla_attn_bf16(
     // A tile that exceeds the reference by more than REF_GAP flags the
     // workgroup, which then reruns the pass with m_ref = the exact max it
     // recorded (so every exponential is <= 1).
-    f32x16 o[DV / 32];
+    //
+    // O: the wave's 128 value columns 128*wave .. +127 of all 128 heads,
+    // 4 x 4 blocks of 32 heads x 32 columns (block (hb, cb) in o[hb][cb]).
+    f32x16 o[4][4];
     float m_ref = -__builtin_inff(), m_all = -__builtin_inff(), l_part = 0.f;
     bool over = false;
-    if (tid == 0) s_redo = 0;
 
     // Per-lane LDS offsets inside a stage (the same for every tile).
     // Key fragment of step ks (A operand: key row hl, features 16ks + 8hh):
@@ -194,6 +206,8 @@ void sparse_mla_attn_bf16(
     // i.e. chunk 4nb + 2gc + (m%4)/2, and receives column 32nb + 16gc + m of
     // the four rows.  lat_swz of those rows is 4(m/4) + ((2j + hh) & 3),
     // independent of kk; slot = 16*(nb/4) + ((4(nb%4) + 2gc + (m%4)/2) ^ f).
+    // The wave's column blocks are nb = 4*wave + cb: the 256-byte group
+    // nb/4 = wave, and nb%4 = cb.
     int v_off[2][4];
     {
         const int m = lane & 15, gc = (lane >> 4) & 1;
@@ -203,7 +217,7 @@ void sparse_mla_attn_bf16(
             const int f = lat_swz(r);
 #pragma unroll
             for (int nq = 0; nq < 4; ++nq)
-                v_off[j][nq] = r * LAT + 16 * ((4 * nq + 2 * gc + ((m & 3) >> 1)) ^ f) + 8 * (m & 1);
+                v_off[j][nq] = r * LAT + 256 * wave + 16 * ((4 * nq + 2 * gc + ((m & 3) >> 1)) ^ f) + 8 * (m & 1);
         }
     }
     const unsigned ring_base = lds_addr(ring);
@@ -225,12 +239,11 @@ void sparse_mla_attn_bf16(
     const i32x4 kv_rsrc = buffer_rsrc(kv_b, (unsigned)N * (unsigned)(2 * DQK));
     const int lane16 = lane << 4;
     auto gather_id = [&](int tile) __attribute__((always_inline)) {
-        // (the lookahead reaches four tiles past the last one: sidx holds
-        // -1 there, and such tiles are never gathered)
+        if (tile >= n_tiles) return -1;
         const int r = 8 * wave + (lane >> 3);
         int id = sidx[tile * TK + r];
         if (id < 0 || id >= N) id = dummy;
-        return tile < n_tiles ? id : -1;
+        return id;
     };
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     auto dma = [&](int tile, int id, int u) __attribute__((always_inline)) {
@@ -252,18 +265,15 @@ void sparse_mla_attn_bf16(
 #pragma unroll
         for (int u = 0; u < DMA_PER_TILE; ++u) dma(tile, id, u);
     };
-    // (the per-lane address parts go through an empty asm statement at each
-    // use, so that the compiler computes every address next to its read --
-    // two VALU operations -- instead of keeping one register per step)
     auto kfrag = [&](const uint8_t* st, int ks) __attribute__((always_inline)) -> bf16x8 {
         const uint8_t* p = ks < 32 ? st + k_off[ks & 7] + 256 * (ks >> 3) : st + r_off[ks - 32];
         return as_bf16x8(*reinterpret_cast<const uint4*>(p));
     };
-    // a tile barrier that is also a compiler memory barrier (no LDS access
-    // moves across it) but, unlike __syncthreads(), waits for no global loads
-    // (its own earlier LDS reads are finished first, so no stage a wave is
-    // still reading gets refilled)
-    auto tile_barrier = [&]() __attribute__((always_inline)) {
+    // a workgroup barrier that is also a compiler memory barrier (no LDS
+    // access moves across it) but, unlike __syncthreads(), waits for no
+    // global loads (its own earlier LDS reads are finished first, so no stage
+    // or P a wave is still reading gets overwritten)
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
@@ -297,10 +307,6 @@ void sparse_mla_attn_bf16(
         for (int i = 0; i < 16; ++i) sacc[i] += s_odd[i];
     };
 
-    // Softmax of tile `tile` (S^T in s, turned into the weights in place),
-    // in NS pieces so that it can run in the shadow of other work; piece j of
-    // NS = 20 after each call of step(j).  The weights end up as bf16 A
-    // operands in pa (k step kk = accumulator registers 8kk .. 8kk+7).
     // Softmax of tile `tile` (S^T in s, turned into the weights in place), in
     // pieces so that it can run in the shadow of other work.  The max runs
     // over all 32 raw logits: a slot that is not valid gathered the dummy
@@ -310,6 +316,8 @@ void sparse_mla_attn_bf16(
     // monotonic in s; NEG: -max(-s) * scale for a negative one); each weight
     // is exp2(fma(s, scale, -m)), and the weights of slots that are not valid
     // are set to 0.  Only tiles with an invalid slot read the slot indices.
+    // The weights end up as bf16 A operands in pa (k step kk = accumulator
+    // registers 8kk .. 8kk+7).
     struct Soft {
         unsigned okm;
         float mx, mr;
@@ -318,7 +326,7 @@ void sparse_mla_attn_bf16(
         sf.mx = -__builtin_inff();
         sf.mr = 0.f;
         unsigned okm = 0xffffu;
-        if ((s_notfull[tile >> 5] >> (tile & 31)) & 1u) {
+        if ((((tile < 32) ? nf0 : nf1) >> (tile & 31)) & 1u) {
             // validity of this lane's keys 8j + 4hh + {0..3}, j = 0..3, as a mask
             okm = 0;
 #pragma unroll
@@ -368,35 +376,60 @@ void sparse_mla_attn_bf16(
         }
     };
 
-    // O[head, v] += P V over tile `tile` (weights pa); when SOFT, the pieces
+    // The wave's P (its 32 heads = head block `wave`) into the shared buffer:
+    // A operand (head block hb, k step kk) of lane l at 16-byte slot
+    // (2 hb + kk) * 64 + l, exactly the registers the softmax left in lane l.
+    auto write_p = [&](const bf16x8* pa) __attribute__((always_inline)) {
+        uint4* pw = reinterpret_cast<uint4*>(pbuf) + 2 * wave * 64 + lane;
+        pw[0] = __builtin_bit_cast(uint4, pa[0]);
+        pw[64] = __builtin_bit_cast(uint4, pa[1]);
+    };
+
+    // O[head, v] += P V over tile `tile` for the wave's 128 value columns and
+    // all four head blocks (P from the shared buffer); when SOFT, the pieces
     // of the next tile's softmax (on sn, into pn) run between the MFMAs.
-    // Value fragments are read three steps ahead.
-    auto pv = [&](int tile, const bf16x8* pa, auto soft_t, f32x16& sn, Soft& sf, bf16x8* pn)
-        __attribute__((always_inline)) {
+    // Value fragments of k step 0 are read first, those of k step 1 during
+    // the second half of step 0; each P fragment one head block ahead.
+    auto pv = [&](int tile, auto soft_t, f32x16& sn, Soft& sf, bf16x8* pn) __attribute__((always_inline)) {
         constexpr bool SOFT = decltype(soft_t)::value;
         const uint8_t* st = stage_of(tile);
-        auto vfrag = [&](int s) __attribute__((always_inline)) -> bf16x8 {
-            const int kk = s >> 4, nb = s & 15;
-            const uint8_t* base = st + kk * 16 * LAT + 256 * (nb >> 2);
-            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[0][nb & 3]));
-            const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[1][nb & 3]));
+        const uint4* pr = reinterpret_cast<const uint4*>(pbuf) + lane;
+        auto vfrag = [&](int kk, int cb) __attribute__((always_inline)) -> bf16x8 {
+            const uint8_t* base = st + kk * 16 * LAT;
+            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[0][cb]));
+            const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + v_off[1][cb]));
             const uint4 vv = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 0, 1)),
                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(c, c, 2, 3))};
             return as_bf16x8(vv);
         };
-        constexpr int VD = 2;  // prefetch distance
-        bf16x8 vf[VD + 1];
+        auto afrag = [&](int hb, int kk) __attribute__((always_inline)) -> bf16x8 {
+            return as_bf16x8(pr[(2 * hb + kk) * 64]);
+        };
+        bf16x8 vb[2][4], pf[2];
 #pragma unroll
-        for (int s = 0; s < VD; ++s) vf[s] = vfrag(s);
+        for (int cb = 0; cb < 4; ++cb) vb[0][cb] = vfrag(0, cb);
+        pf[0] = afrag(0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 2 * (DV / 32); ++s) {
-            if (s + VD < 2 * (DV / 32)) vf[(s + VD) % (VD + 1)] = vfrag(s + VD);
-            o[s & 15] = mfma32(pa[s >> 4], vf[s % (VD + 1)], o[s & 15]);
-            if (SOFT && s < 19) soft_piece(s, sn, sf, pn);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                const int step = 4 * kk + hb;
+                if (step + 1 < 8) pf[(step + 1) & 1] = afrag((hb + 1) & 3, kk + ((hb + 1) >> 2));
+                if (kk == 0 && hb == 2) {
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) vb[1][cb] = vfrag(1, cb);
+                }
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    o[hb][cb] = mfma32(pf[step & 1], vb[kk][cb], o[hb][cb]);
+                    const int s = 4 * step + cb;
+                    if (SOFT && s < 19) soft_piece(s, sn, sf, pn);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
     };
 
@@ -409,14 +442,18 @@ void sparse_mla_attn_bf16(
     DSA_WAIT_VM(0);
 
     // Pipeline of a pass: tile t's S^T on the MFMA pipe; then tile t-1's
-    // P V on the MFMA pipe with tile t's softmax on the VALU in its shadow.
-    // Tile t + 2 is gathered during tile t's S^T into the stage of tile t-2,
-    // which every wave has finished with at tile t's barrier.
+    // P V on the MFMA pipe with tile t's softmax on the VALU in its shadow;
+    // then, once every wave has read tile t-1's P, tile t's P goes into the
+    // shared buffer.  Tile t + 2 is gathered during tile t's S^T into the
+    // stage of tile t-2, which every wave has finished with at tile t's
+    // barrier.
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int i = 0; i < DV / 32; ++i)
+        for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[hb][cb][e] = 0.f;
         l_part = 0.f;
         m_ref = pass == 0 ? -__builtin_inff() : m_all;
         if (pass == 0) m_all = -__builtin_inff();
@@ -427,34 +464,43 @@ void sparse_mla_attn_bf16(
         if (n_tiles > 0) {
             f32x16 s;
             Soft sf;
-            bf16x8 pa[2], pn[2];
+            bf16x8 pa[2];
             // tile 0 (tile 1's loads may stay in flight)
             DSA_WAIT_VM(DMA_PER_TILE);
-            tile_barrier();
+            lds_barrier();
             qk(0, s);
             soft_begin(0, sf);
 #pragma unroll
             for (int j = 0; j < 19; ++j) soft_piece(j, s, sf, pa);
+            write_p(pa);
             for (int it = 1; it < n_tiles; ++it) {
                 DSA_WAIT_VM(DMA_PER_TILE);
-                tile_barrier();
+                lds_barrier();  // tile it is in, and every wave's P of tile it-1
                 qk(it, s);
                 soft_begin(it, sf);
-                pv(it - 1, pa, std::true_type{}, s, sf, pn);
-                pa[0] = pn[0];
-                pa[1] = pn[1];
+                pv(it - 1, std::true_type{}, s, sf, pa);
+                lds_barrier();  // every wave is done with tile it-1's P
+                write_p(pa);
             }
-            pv(n_tiles - 1, pa, std::false_type{}, s, sf, pn);
+            lds_barrier();
+            pv(n_tiles - 1, std::false_type{}, s, sf, pa);
         }
         DSA_WAIT_VM(0);  // the loads past the last tile land before the stages are reused
         if (pass == 1) break;
         m_all = fmaxf(m_all, __shfl_xor(m_all, 32, 64));  // per-lane maxima -> max of the head
-        if (__any(over) && lane == 0) atomicOr(&s_redo, 1);
+        // (s_redo shares the P buffer: every wave is done with it first)
         __syncthreads();
-        if (s_redo == 0) break;
+        if (tid == 0) *s_redo = 0;
+        __syncthreads();
+        if (__any(over) && lane == 0) atomicOr(s_redo, 1);
+        __syncthreads();
+        const bool redo = *s_redo != 0;
+        __syncthreads();
+        if (!redo) break;
     }
 
-    // ---- finish: exp-sum of the lane's head (both halves), then per O row
+    // ---- finish: exp-sum of the lane's head (both halves); every head's
+    // exp-sum through LDS to the waves that hold its O columns
     const int h0 = 32 * wave;
     const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (PARTIAL) {
@@ -467,30 +513,37 @@ void sparse_mla_attn_bf16(
     } else if (lse != nullptr && hh == 0) {
         lse[row * H + h0 + hl] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -__builtin_inff();
     }
-    // O register i of column block nb holds head 8(i/4) + 4hh + i%4, column
-    // 32nb + hl: the exp-sums of those heads come from the lanes that own them
-    float inv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float li = __shfl(l_tot, 8 * (i >> 2) + 4 * hh + (i & 3), 64);
-        inv[i] = li > 0.f ? 1.f / li : 0.f;
-    }
-    // normalise, stage the wave's 32 x 512 bf16 block (32 KiB) in its own ring
-    // stage and store it with 16-byte writes
+    __syncthreads();  // (s_l shares the P buffer)
+    if (hh == 0) s_l[h0 + hl] = l_tot;
     __syncthreads();
+    // o[hb][cb] register i holds head 32hb + 8(i/4) + 4hh + i%4, column
+    // 128 wave + 32 cb + hl; normalise and stage the wave's 128 x 128 bf16
+    // block (32 KiB) in its own ring stage, then store it with 16-byte writes
     uint16_t* ob = reinterpret_cast<uint16_t*>(ring + wave * STAGE);
 #pragma unroll
-    for (int nb = 0; nb < DV / 32; ++nb)
+    for (int hb = 0; hb < 4; ++hb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            ob[(8 * (i >> 2) + 4 * hh + (i & 3)) * DV + 32 * nb + hl] =
-                __builtin_bit_cast(uint16_t, (__bf16)(o[nb][i] * inv[i]));
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const float4 lv = *reinterpret_cast<const float4*>(&s_l[32 * hb + 8 * i4 + 4 * hh]);
+            const float la[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float inv = la[e] > 0.f ? 1.f / la[e] : 0.f;
+                const int head = 32 * hb + 8 * i4 + 4 * hh + e;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    ob[head * 128 + 32 * cb + hl] = __builtin_bit_cast(uint16_t, (__bf16)(o[hb][cb][4 * i4 + e] * inv));
+            }
+        }
+    }
     __syncthreads();
-    uint16_t* dst = PARTIAL ? part_o + ((row * nsplit + split) * H + h0) * DV : out + (row * H + h0) * DV;
+    uint16_t* dst = PARTIAL ? part_o + (row * nsplit + split) * H * DV : out + row * H * DV;
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-        const int c = r * 64 + lane;  // 16-byte chunk of the wave's block
-        *reinterpret_cast<uint4*>(dst + c * 8) = *reinterpret_cast<const uint4*>(ob + c * 8);
+        const int c = r * 64 + lane;  // 16-byte chunk of the wave's block: head c/16, piece c%16
+        const int head = c >> 4, piece = c & 15;
+        *reinterpret_cast<uint4*>(dst + head * DV + 128 * wave + 8 * piece) =
+            *reinterpret_cast<const uint4*>(ob + head * 128 + 8 * piece);
     }
 }
 
