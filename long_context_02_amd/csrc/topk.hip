@@ -6,7 +6,10 @@
 // index, -0 equals +0, NaN ranks lowest; the kept indices are written in
 // ascending order and padded with -1.
 //
-// One 1024-thread workgroup per row, radix select on an order-preserving
+// Rows of at most 32768 candidates (prefill) are selected from registers by
+// the register-resident selection below.  Longer rows: one 1024-thread
+// workgroup per row (a sampled-threshold one-pass filter, or, when its sample
+// misleads, the two-pass selection), radix select on an order-preserving
 // 32-bit key:
 //   pass 1 (HBM)  LDS histogram of the top 12 key bits -> the bin b1 holding
 //                 the k-th largest key, the count above it and in it;
@@ -47,12 +50,15 @@ constexpr int WREG = 384;              // candidate slots per wave
 constexpr int CAP1 = WREG * NW;        // 6144
 constexpr int ONEPASS_LDS_WORDS = 2 * CAP1 + BINS + NW + 1 + 3 + NW + 1;
 constexpr int ROWS_LDS_WORDS = ONEPASS_LDS_WORDS > ROW_LDS_WORDS ? ONEPASS_LDS_WORDS : ROW_LDS_WORDS;
+// candidate counts of the two register-resident selections (threads x keys)
+constexpr int SHORT_A = 256 * 32, SHORT_B = 512 * 64;
+static_assert(SHORT_B <= 16 * SAMP, "rows past the register-resident range take the one-pass path");
 
 __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores,
                                                 int32_t* __restrict__ idx, int T, int N, int k,
-                                                int q_offset) {
+                                                int q_offset, int t0) {
     __shared__ uint32_t lds[ROWS_LDS_WORDS];
-    const int t = blockIdx.x, b = blockIdx.y;
+    const int t = t0 + (int)blockIdx.x, b = blockIdx.y;
     const size_t row = (size_t)b * T + t;
     const int n_cand = (int)min((long long)N, (long long)q_offset + t + 1);
     int32_t* __restrict__ out = idx + row * k;
@@ -135,6 +141,310 @@ __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores
         return;
     }
     select_candidates<TT, true>(ckey, cidx, CAP1, k, n_cand, out, hist, sh, res);
+}
+
+// ---------------------------------------------------------------------------
+// Rows of at most NTR * PER candidates (prefill rows): the row is read from
+// HBM once, into registers -- thread tid holds the 4 consecutive keys at
+// 4 (j NTR + tid) for j < PER / 4, so token order is (j, thread, c) -- and
+// everything after the load works on those registers:
+//   range         the smallest and largest key other than 0 (NaN) and the
+//                 number of such keys; with fewer than k of them K* = 0;
+//   digits        keys are taken relative to the smallest one, so the first
+//                 digit's 4096 bins span just the row's range; LDS
+//                 histograms of that digit and of 10-bit digits below it
+//                 among the keys that still share the k-th key's prefix give
+//                 the k-th key K* and r, the number of keys equal to K* to
+//                 keep (lowest indices first); when the k-th key's bin holds
+//                 exactly the keys still needed, every key of that bin is
+//                 kept and the later digits are skipped;
+//   placement     per (j, thread) the count of keys > K* and of keys == K*,
+//                 a wave scan of the two counts per j and a block scan over
+//                 the (j, wave) totals give every key the number of picks
+//                 before it in token order, i.e. its output slot; the picks
+//                 are gathered in LDS and written out with 16-byte stores.
+// Wave scans and reductions use DPP row shifts and row broadcasts.  A
+// workgroup holds one row; short rows use few threads, so several rows share
+// a CU and one row's loads overlap another row's LDS steps (WPE: the waves
+// per SIMD the register budget is cut for -- 8 for 256 threads x 32 keys,
+// 4 for 512 threads x 64 keys, i.e. eight and two rows per CU).
+
+// Inclusive scan over the 64 lanes of a wave with op (DPP: row_shr 1, 2, 4, 8
+// within rows of 16 lanes, then row_bcast 15 and 31 across rows).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, Op op) {
+    const int lane = threadIdx.x & 63, rl = lane & 15;
+    uint32_t t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);
+    if (rl >= 1) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);
+    if (rl >= 2) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);
+    if (rl >= 4) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);
+    if (rl >= 8) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);
+    if ((lane & 31) >= 16) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);
+    if (lane >= 32) v = op(v, t);
+    return v;
+}
+struct AddOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MinOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Exclusive prefix sum over the NTR threads in thread order; *total gets the
+// sum.  sh: NTR / 64 + 1 words.  Barriers inside: every thread calls it.
+template <int NTR>
+__device__ __forceinline__ uint32_t block_scan_dpp(uint32_t v, uint32_t* sh, uint32_t* total) {
+    constexpr int NWR = NTR / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_scan_dpp(v, AddOp{});
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NWR; ++w) {
+        const uint32_t x = sh[w];
+        before += w < wave ? x : 0u;
+        all += x;
+    }
+    *total = all;
+    __syncthreads();
+    return before + incl - v;
+}
+
+// The bin of the need-th largest element over nb bins (read from the top):
+// (bin, count above it, count in it) into res.  Barriers inside.
+template <int NTR>
+__device__ __forceinline__ void find_bin_dpp(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh,
+                                             uint32_t* res) {
+    const int per = nb / NTR;  // bins per thread: [hi - per, hi)
+    const int hi = nb - per * (int)threadIdx.x;
+    uint32_t cnt = 0;
+    for (int i = 1; i <= per; ++i) cnt += hist[hi - i];
+    uint32_t total;
+    const uint32_t above = block_scan_dpp<NTR>(cnt, sh, &total);
+    if (cnt > 0 && above < need && above + cnt >= need) {
+        uint32_t acc = above;
+        for (int i = 1; i <= per; ++i) {
+            const uint32_t h = hist[hi - i];
+            if (acc + h >= need) {
+                res[0] = (uint32_t)(hi - i);
+                res[1] = acc;
+                res[2] = h;
+                break;
+            }
+            acc += h;
+        }
+    }
+    __syncthreads();
+}
+
+template <int NTR, int PER, int WPE>
+__global__ __launch_bounds__(NTR, WPE) void topk_short_rows(const float* __restrict__ scores,
+                                                       int32_t* __restrict__ idx, int T, int N, int k,
+                                                       int q_offset, int t0) {
+    constexpr int NWR = NTR / 64, J = PER / 4, GROUPS = J * NWR;
+    static_assert(GROUPS <= NTR && BINS % NTR == 0 && 1024 % NTR == 0, "work per thread");
+    static_assert(BINS >= KMAX, "the picks are gathered in the histogram's words");
+    __shared__ __align__(16) uint32_t hist[BINS];
+    __shared__ uint32_t gsum[GROUPS];
+    __shared__ uint32_t sh[NWR + 1];
+    __shared__ uint32_t res[3];
+    __shared__ uint32_t rng[3 * NWR];
+    const int t = t0 + (int)blockIdx.x, b = blockIdx.y;
+    const size_t row = (size_t)b * T + t;
+    const int n_cand = (int)min((long long)N, (long long)q_offset + t + 1);
+    int32_t* __restrict__ out = idx + row * k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (n_cand <= k) {  // every candidate is kept
+        for (int i = tid; i < k; i += NTR) out[i] = i < n_cand ? i : -1;
+        return;
+    }
+    const float* __restrict__ s = scores + row * N;
+    const bool vec = ((reinterpret_cast<uintptr_t>(s) & 15u) == 0);
+    // groups j < nj hold candidates; positions at or past n_cand get key 0,
+    // the key of NaN, the lowest: they come after every candidate in token
+    // order, so as ties of key 0 they are never among the kept ones
+    const int nj = (n_cand + 4 * NTR - 1) / (4 * NTR);
+    // buffer loads over the row's candidates: a 4-byte load past them
+    // returns 0 and touches no memory (a 16-byte load is only issued when it
+    // lies wholly inside)
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s), 0, 4 * n_cand, 0x00020000);
+    uint32_t key[J][4];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if (j < nj) {
+            const int off = 16 * (j * NTR + tid);
+            if (vec && 4 * (j * NTR + tid) + 4 <= n_cand) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[j][c] = x[c];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[j][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * c, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) key[j][c] = 0u;
+        }
+    }
+    // ---- range of the keys other than 0
+    uint32_t lo = 0xffffffffu, hi = 0u, nz = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if (j >= nj) continue;
+        const int e = 4 * (j * NTR + tid);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t kk = e + c < n_cand ? fkey(__uint_as_float(key[j][c])) : 0u;
+            key[j][c] = kk;
+            if (kk != 0u) {
+                lo = min(lo, kk);
+                hi = max(hi, kk);
+                ++nz;
+            }
+        }
+    }
+    lo = lane63(wave_scan_dpp(lo, MinOp{}));
+    hi = lane63(wave_scan_dpp(hi, MaxOp{}));
+    nz = lane63(wave_scan_dpp(nz, AddOp{}));
+    if (lane == 0) {
+        rng[3 * wave] = lo;
+        rng[3 * wave + 1] = hi;
+        rng[3 * wave + 2] = nz;
+    }
+    __syncthreads();
+    lo = 0xffffffffu;
+    hi = 0u;
+    nz = 0u;
+#pragma unroll
+    for (int w = 0; w < NWR; ++w) {
+        lo = min(lo, rng[3 * w]);
+        hi = max(hi, rng[3 * w + 1]);
+        nz += rng[3 * w + 2];
+    }
+
+    // ---- digits: K* = kthr, r = keys == K* still to take
+    // Keys other than 0 are rebased to key - lo + 1 (order kept, 0 stays the
+    // lowest); the first digit is their bits shift.. (at most 12 bits).  The
+    // lanes past n_cand skip the histograms; the z keys of 0 the others hold
+    // (NaN, and the padding after the last candidate) land in bin 0 of every
+    // digit whose prefix is 0 and are taken out of it again.
+    uint32_t kthr = 0u, r = (uint32_t)k - nz;  // fewer than k keys other than 0: K* = 0
+    if (nz >= (uint32_t)k) {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) key[j][c] = key[j][c] != 0u ? key[j][c] - lo + 1u : 0u;
+        const uint32_t top = hi - lo + 1u;
+        int shift = max(0, 32 - __clz(top) - 12);
+        const uint32_t z = (uint32_t)(n_cand + ((4 - (n_cand & 3)) & 3)) - nz;
+        for (int i = tid; i < BINS; i += NTR) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (j < nj && 4 * (j * NTR + tid) < n_cand)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) atomicAdd(&hist[key[j][c] >> shift], 1u);
+        __syncthreads();
+        if (tid == 0) hist[0] -= z;
+        __syncthreads();
+        find_bin_dpp<NTR>(hist, BINS, (uint32_t)k, sh, res);
+        uint32_t prefix = res[0], need = (uint32_t)k - res[1], in_bin = res[2];
+        // while the bin does not hold exactly the keys still needed, the
+        // next digit (at most 10 bits) among the keys of the bin; when it
+        // does, the whole bin is kept: every key >= its lowest key
+        while (shift > 0 && in_bin != need) {
+            const int d = min(10, shift);
+            for (int i = tid; i < 1024; i += NTR) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (j < nj && 4 * (j * NTR + tid) < n_cand)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if ((key[j][c] >> shift) == prefix)
+                            atomicAdd(&hist[(key[j][c] >> (shift - d)) & ((1u << d) - 1u)], 1u);
+            __syncthreads();
+            if (prefix == 0u) {
+                if (tid == 0) hist[0] -= z;
+                __syncthreads();
+            }
+            find_bin_dpp<NTR>(hist, 1024, need, sh, res);
+            prefix = (prefix << d) | res[0];
+            need -= res[1];
+            in_bin = res[2];
+            shift -= d;
+        }
+        kthr = prefix << shift;
+        r = shift == 0 ? need : 0xffffffffu;
+    }
+
+    // ---- placement: picks are keys > kthr, and keys == kthr while fewer
+    // than r of them came before
+    uint32_t ex[J];  // per j: (keys > kthr) | (keys == kthr) << 16 before this thread's 4, in the wave
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if (j < nj) {
+            uint32_t g = 0, q = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                g += key[j][c] > kthr;
+                q += key[j][c] == kthr;
+            }
+            const uint32_t mine = g | (q << 16);
+            const uint32_t incl = wave_scan_dpp(mine, AddOp{});
+            ex[j] = incl - mine;
+            if (lane == 63) gsum[j * NWR + wave] = incl;
+        } else {
+            ex[j] = 0u;
+            if (lane == 63) gsum[j * NWR + wave] = 0u;
+        }
+    }
+    __syncthreads();
+    {
+        const uint32_t v = tid < GROUPS ? gsum[tid] : 0u;
+        uint32_t total;
+        const uint32_t before = block_scan_dpp<NTR>(v, sh, &total);
+        if (tid < GROUPS) gsum[tid] = before;
+        __syncthreads();
+    }
+    int32_t* picks = reinterpret_cast<int32_t*>(hist);  // k slots (the histograms are done)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if (j >= nj) continue;
+        const uint32_t base = gsum[j * NWR + wave] + ex[j];
+        uint32_t gb = base & 0xffffu, tb = base >> 16;
+        const int e = 4 * (j * NTR + tid);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (key[j][c] > kthr) {
+                picks[gb + min(tb, r)] = e + c;
+                ++gb;
+            } else if (key[j][c] == kthr) {
+                if (tb < r) picks[gb + tb] = e + c;
+                ++tb;
+            }
+        }
+    }
+    __syncthreads();
+    if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+        for (int i = 4 * tid; i < k; i += 4 * NTR)
+            *reinterpret_cast<int4*>(out + i) = *reinterpret_cast<const int4*>(picks + i);
+    } else {
+        for (int i = tid; i < k; i += NTR) out[i] = picks[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -446,8 +756,25 @@ dsa_status launch_topk(const float* scores, int32_t* idx, int B, int T, int N, i
     if (B > 65535) return DSA_ERR_UNSUPPORTED;
     const long long rows = (long long)B * T;
     if (!topk_segmented(rows)) {
-        DSA_TIMED("topk_rows", stream,
-                  topk_rows<<<dim3(T, B), TT, 0, stream>>>(scores, idx, T, N, k, q_offset));
+        // rows in token order have non-decreasing candidate counts: rows of at
+        // most 8192 and of at most 32768 candidates go to the register-resident
+        // selection, longer ones to the one-pass selection
+        auto rows_upto = [&](long long limit) -> int {
+            if (N <= limit) return T;
+            return (int)std::max<long long>(0, std::min<long long>(T, limit - q_offset));
+        };
+        const int t_a = rows_upto(SHORT_A), t_b = rows_upto(SHORT_B);
+        if (t_a > 0)
+            DSA_TIMED("topk_short_rows<256, 32>", stream,
+                      (topk_short_rows<256, 32, 8><<<dim3(t_a, B), 256, 0, stream>>>(scores, idx, T, N, k,
+                                                                                    q_offset, 0)));
+        if (t_b > t_a)
+            DSA_TIMED("topk_short_rows<512, 64>", stream,
+                      (topk_short_rows<512, 64, 4><<<dim3(t_b - t_a, B), 512, 0, stream>>>(scores, idx, T, N,
+                                                                                          k, q_offset, t_a)));
+        if (T > t_b)
+            DSA_TIMED("topk_rows", stream,
+                      topk_rows<<<dim3(T - t_b, B), TT, 0, stream>>>(scores, idx, T, N, k, q_offset, t_b));
         return launch_status();
     }
     // few long rows: several workgroups per row

@@ -49,9 +49,10 @@ def test_random_rows(B, T, N, k, q_offset):
     _check(s, k, q_offset, f"random B={B} T={T} N={N} k={k}")
 
 
-def test_ties_zeros_signed_zero_nan():
+@pytest.mark.parametrize("N", [6000, 20000])
+def test_ties_zeros_signed_zero_nan(N):
     g = _gen(5)
-    T, N = 32, 6000
+    T = 32
     s = torch.randint(0, 4, (1, T, N), generator=g).float() * 0.5  # heavy exact ties
     s[torch.rand(1, T, N, generator=g) < 0.3] = 0.0
     s[torch.rand(1, T, N, generator=g) < 0.1] = -0.0
@@ -80,6 +81,19 @@ def test_decode_rows_ties_and_one_bin():
     s[0, 2] = 0.5                               # one value everywhere
     s[0, 3] = 1.0 + torch.rand(N, generator=g) * 0.1  # all keys in one bin
     _check(s, 2048, N - 4, "decode ties")
+
+
+@pytest.mark.parametrize("B,T,N,k,q_offset", [
+    (1, 400, 8400, 2048, 7999),     # rows on both sides of 8192 candidates
+    (1, 300, 33000, 2048, 32700),   # rows on both sides of 32768 candidates
+    (1, 2600, 2600, 2048, 0),       # causal prefill from one candidate
+    (1, 260, 32768, 700, 32508),    # up to exactly 32768 candidates, k = 700
+])
+def test_prefill_row_length_ranges(B, T, N, k, q_offset):
+    """Rows of a prefill batch go to the selection for their candidate count
+    (at most 8192, at most 32768, longer); each range and its edges."""
+    s = torch.randn(B, T, N, generator=_gen(T + N)).abs()
+    _check(s, k, q_offset, f"ranges B={B} T={T} N={N} k={k}")
 
 
 def test_negative_and_infinite_scores():
