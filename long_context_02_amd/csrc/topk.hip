@@ -387,7 +387,9 @@ __global__ __launch_bounds__(NTR, WPE) void topk_short_rows(const float* __restr
             in_bin = res[2];
             shift -= d;
         }
-        kthr = prefix << shift;
+        // (a bin kept whole starts at its lowest key; the lowest bin's lowest
+        // key other than 0 is 1)
+        kthr = shift == 0 ? prefix : max(prefix << shift, 1u);
         r = shift == 0 ? need : 0xffffffffu;
     }
 
@@ -710,6 +712,161 @@ __device__ void rescore_row(const uint8_t* __restrict__ q, const float* __restri
     }
 }
 
+// The need-th largest of the values of v other than 0 (v: P per thread of a
+// TT-thread workgroup; 0 marks "not a value"), in registers.  The values are
+// rebased in place to v - lo + 1 (order kept, 0 stays 0; lo = the smallest
+// value) and *thr gets the need-th largest rebased value, *r how many values
+// equal to it to keep (0xffffffff: all of them; the bin they share is kept
+// whole).  With fewer than need values, *thr = 0 and *r = need - count (the
+// caller's 0 entries make up the rest).  hist: BINS words; sh: NW + 1;
+// res: 3; rng: 3 NW.  Barriers inside: every thread calls it.
+template <int P>
+__device__ void kth_largest_rebased(uint32_t (&v)[P], uint32_t need, uint32_t* hist, uint32_t* sh,
+                                    uint32_t* res, uint32_t* rng, uint32_t* thr, uint32_t* r) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t lo = 0xffffffffu, hi = 0u, nz = 0u;
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (v[j] != 0u) {
+            lo = min(lo, v[j]);
+            hi = max(hi, v[j]);
+            ++nz;
+        }
+    lo = lane63(wave_scan_dpp(lo, MinOp{}));
+    hi = lane63(wave_scan_dpp(hi, MaxOp{}));
+    nz = lane63(wave_scan_dpp(nz, AddOp{}));
+    if (lane == 0) {
+        rng[3 * wave] = lo;
+        rng[3 * wave + 1] = hi;
+        rng[3 * wave + 2] = nz;
+    }
+    __syncthreads();
+    lo = 0xffffffffu;
+    hi = 0u;
+    nz = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        lo = min(lo, rng[3 * w]);
+        hi = max(hi, rng[3 * w + 1]);
+        nz += rng[3 * w + 2];
+    }
+    __syncthreads();  // (rng is reused by the next call)
+#pragma unroll
+    for (int j = 0; j < P; ++j) v[j] = v[j] != 0u ? v[j] - lo + 1u : 0u;
+    if (nz < need) {
+        *thr = 0u;
+        *r = need - nz;
+        return;
+    }
+    int shift = max(0, 32 - __clz(hi - lo + 1u) - 12);
+    for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (v[j] != 0u) atomicAdd(&hist[v[j] >> shift], 1u);
+    __syncthreads();
+    find_bin_dpp<TT>(hist, BINS, need, sh, res);
+    uint32_t prefix = res[0], in_bin = res[2];
+    need -= res[1];
+    while (shift > 0 && in_bin != need) {
+        const int d = min(10, shift);
+        for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            if (v[j] != 0u && (v[j] >> shift) == prefix)
+                atomicAdd(&hist[(v[j] >> (shift - d)) & ((1u << d) - 1u)], 1u);
+        __syncthreads();
+        find_bin_dpp<TT>(hist, 1024, need, sh, res);
+        prefix = (prefix << d) | res[0];
+        need -= res[1];
+        in_bin = res[2];
+        shift -= d;
+    }
+    *thr = shift == 0 ? prefix : max(prefix << shift, 1u);
+    *r = shift == 0 ? need : 0xffffffffu;
+}
+
+// Exact top-k of a row from its candidate list (n_c >= k keys and token
+// indices in the workspace, any order; every key >= the row's k-th key is in
+// it), selected in registers -- 12 candidates per thread: the k-th key and
+// the number of its ties to keep (kth_largest_rebased), among the ties the
+// lowest indices (the same selection on the inverted indices), then the picks
+// in ascending index order through a bitmap over windows of BM_BITS token
+// indices and a block scan of the per-thread bit counts.
+__device__ void select_cands_reg(const uint32_t* __restrict__ wr, int n_c, int k, int n_cand,
+                                 int32_t* __restrict__ out, uint32_t* hist, uint32_t* sh, uint32_t* res,
+                                 uint32_t* rng) {
+    constexpr int P = CAPG / TT;
+    static_assert(CAPG % TT == 0 && BINS % TT == 0, "work per thread");
+    const int tid = threadIdx.x;
+    uint32_t key[P], inv[P];
+    int32_t cid[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int i = tid + j * TT;
+        key[j] = i < n_c ? wr[WS_CKEY + i] : 0u;
+        cid[j] = i < n_c ? (int32_t)wr[WS_CIDX + i] : -1;
+    }
+    // keys of 0 (NaN) are candidates too: they are the lowest, and the caller
+    // checked n_c >= k, so kth_largest_rebased's "fewer than k" case leaves
+    // r ties among them
+    uint32_t kthr, r;
+    kth_largest_rebased<P>(key, (uint32_t)k, hist, sh, res, rng, &kthr, &r);
+    // ties of key kthr beyond the r to keep: the r lowest indices, i.e. the
+    // r largest inverted indices
+    uint32_t n_tie = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) n_tie += cid[j] >= 0 && key[j] == kthr;
+    n_tie = lane63(wave_scan_dpp(n_tie, AddOp{}));
+    if ((tid & 63) == 0) rng[tid >> 6] = n_tie;
+    __syncthreads();
+    n_tie = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n_tie += rng[w];
+    __syncthreads();
+    uint32_t ithr = 0u;  // ties kept: inverted (rebased) index >= ithr
+    const bool cut = r != 0xffffffffu && n_tie > r;
+#pragma unroll
+    for (int j = 0; j < P; ++j) inv[j] = cut && cid[j] >= 0 && key[j] == kthr ? ~(uint32_t)cid[j] : 0u;
+    if (cut) {
+        uint32_t r2;
+        kth_largest_rebased<P>(inv, r, hist, sh, res, rng, &ithr, &r2);
+    }
+    // emission in ascending index order
+    uint32_t emitted = 0;
+    for (int w0 = 0; w0 < n_cand; w0 += BM_BITS) {
+        for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const bool take = cid[j] >= 0 && (key[j] > kthr || (key[j] == kthr && (!cut || inv[j] >= ithr)));
+            const int e = cid[j] - w0;
+            if (take && e >= 0 && e < BM_BITS) atomicOr(&hist[e >> 5], 1u << (e & 31));
+        }
+        __syncthreads();
+        constexpr int WPT = BINS / TT;
+        uint32_t m[WPT], cnt = 0;
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            m[j] = hist[WPT * tid + j];
+            cnt += __popc(m[j]);
+        }
+        uint32_t total;
+        uint32_t p = emitted + block_scan_dpp<TT>(cnt, sh, &total);
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            uint32_t x = m[j];
+            while (x) {
+                const int b = __ffs(x) - 1;
+                x &= x - 1u;
+                out[p++] = w0 + 32 * (WPT * tid + j) + b;
+            }
+        }
+        emitted += total;
+    }
+}
+
 __global__ __launch_bounds__(TT) void topk_cand_select(
     const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ kk,
     const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
@@ -733,14 +890,11 @@ __global__ __launch_bounds__(TT) void topk_cand_select(
         select_row(srow, out, n_cand, k, carve_row_lds(lds));
         return;
     }
-    uint32_t* ckey = lds;                                        // CAPG
-    int32_t* cidx = reinterpret_cast<int32_t*>(ckey + CAPG);     // CAPG
-    uint32_t* hist = reinterpret_cast<uint32_t*>(cidx + CAPG);   // BINS, later the bitmap
-    uint32_t* sh = hist + BINS;                                  // NW + 1
-    uint32_t* res = sh + NW + 1;                                 // 3
-    load_candidates(wr, n_c, ckey, cidx);
-    __syncthreads();
-    select_candidates(ckey, cidx, n_c, k, n_cand, out, hist, sh, res);
+    uint32_t* hist = lds;            // BINS, later the bitmap
+    uint32_t* sh = hist + BINS;      // NW + 1
+    uint32_t* res = sh + NW + 1;     // 3
+    uint32_t* rng = res + 3;         // 3 NW
+    select_cands_reg(wr, n_c, k, n_cand, out, hist, sh, res, rng);
 }
 
 }  // namespace

@@ -185,6 +185,23 @@ def test_decode_selection_fallback_few_candidates():
     _forward_vs_separate(wl, g, "few candidates")
 
 
+def test_decode_selection_ties():
+    """Key rows repeated in groups (identical codes and scales) give exact
+    score ties throughout the row, at the k-th key too: the selection from
+    the candidate list keeps the lowest-index ties."""
+    dev = gpu_device()
+    wl = WORKLOADS["decode_128k"].with_(B=3, N=32768, q_offset=32767)
+    g = make_inputs(wl, seed=12, device=dev)
+    N = wl.N
+    for b, src in ((0, torch.arange(N, device=dev) // 37 * 37),                # groups of 37
+                   (1, torch.randint(0, 300, (N,), device=dev,                 # 300 distinct rows
+                                     generator=torch.Generator(device=dev).manual_seed(3)))):
+        g["k_idx"][b] = g["k_idx"][b][src].clone()
+        g["k_idx_scale"][b] = g["k_idx_scale"][b][src].clone()
+    print("[forward] decode selection with tied scores", flush=True)
+    _forward_vs_separate(wl, g, "ties")
+
+
 def test_deterministic():
     dev = gpu_device()
     wl = WORKLOADS["prefill_8k"].with_(T=2048, N=2048, k=512)

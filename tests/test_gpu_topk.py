@@ -96,6 +96,20 @@ def test_prefill_row_length_ranges(B, T, N, k, q_offset):
     _check(s, k, q_offset, f"ranges B={B} T={T} N={N} k={k}")
 
 
+@pytest.mark.parametrize("N", [5000, 9001])
+def test_rows_with_exactly_k_numbers(N):
+    """Rows whose candidates hold exactly k numbers and NaN elsewhere: the
+    k-th largest key is the smallest number, its bin is kept whole, and no
+    NaN may be picked."""
+    g = _gen(21 + N)
+    T, k = 16, 2048
+    s = torch.full((1, T, N), float("nan"))
+    for t in range(T):
+        pos = torch.randperm(N - T + t + 1, generator=g)[:k]
+        s[0, t, pos] = torch.randn(k, generator=g) if t % 2 == 0 else torch.ones(k)
+    _check(s, k, N - T, f"exactly k numbers N={N}")
+
+
 def test_negative_and_infinite_scores():
     g = _gen(7)
     s = torch.randn(1, 16, 4096, generator=g)
