@@ -36,15 +36,245 @@
 namespace dsa {
 namespace {
 
+// Inclusive scan over the 64 lanes of a wave with op (DPP: row_shr 1, 2, 4, 8
+// within rows of 16 lanes, then row_bcast 15 and 31 across rows).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, Op op) {
+    const int lane = threadIdx.x & 63, rl = lane & 15;
+    uint32_t t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);
+    if (rl >= 1) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);
+    if (rl >= 2) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);
+    if (rl >= 4) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);
+    if (rl >= 8) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);
+    if ((lane & 31) >= 16) v = op(v, t);
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);
+    if (lane >= 32) v = op(v, t);
+    return v;
+}
+struct AddOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MinOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxOp {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Exclusive prefix sum over the NTR threads in thread order; *total gets the
+// sum.  sh: NTR / 64 + 1 words.  Barriers inside: every thread calls it.
+template <int NTR>
+__device__ __forceinline__ uint32_t block_scan_dpp(uint32_t v, uint32_t* sh, uint32_t* total) {
+    constexpr int NWR = NTR / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_scan_dpp(v, AddOp{});
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NWR; ++w) {
+        const uint32_t x = sh[w];
+        before += w < wave ? x : 0u;
+        all += x;
+    }
+    *total = all;
+    __syncthreads();
+    return before + incl - v;
+}
+
+// The bin of the need-th largest element over nb bins (read from the top):
+// (bin, count above it, count in it) into res.  Barriers inside.
+template <int NTR>
+__device__ __forceinline__ void find_bin_dpp(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh,
+                                             uint32_t* res) {
+    const int per = nb / NTR;  // bins per thread: [hi - per, hi)
+    const int hi = nb - per * (int)threadIdx.x;
+    uint32_t cnt = 0;
+    for (int i = 1; i <= per; ++i) cnt += hist[hi - i];
+    uint32_t total;
+    const uint32_t above = block_scan_dpp<NTR>(cnt, sh, &total);
+    if (cnt > 0 && above < need && above + cnt >= need) {
+        uint32_t acc = above;
+        for (int i = 1; i <= per; ++i) {
+            const uint32_t h = hist[hi - i];
+            if (acc + h >= need) {
+                res[0] = (uint32_t)(hi - i);
+                res[1] = acc;
+                res[2] = h;
+                break;
+            }
+            acc += h;
+        }
+    }
+    __syncthreads();
+}
+
+// The need-th largest of the values of v other than 0 (v: P per thread of a
+// TT-thread workgroup; 0 marks "not a value"), in registers.  The values are
+// rebased in place to v - lo + 1 (order kept, 0 stays 0; lo = the smallest
+// value) and *thr gets the need-th largest rebased value, *r how many values
+// equal to it to keep (0xffffffff: all of them; the bin they share is kept
+// whole).  With fewer than need values, *thr = 0 and *r = need - count (the
+// caller's 0 entries make up the rest).  hist: BINS words; sh: NW + 1;
+// res: 3; rng: 3 NW.  Barriers inside: every thread calls it.
+template <int P>
+__device__ void kth_largest_rebased(uint32_t (&v)[P], uint32_t need, uint32_t* hist, uint32_t* sh,
+                                    uint32_t* res, uint32_t* rng, uint32_t* thr, uint32_t* r) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t lo = 0xffffffffu, hi = 0u, nz = 0u;
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (v[j] != 0u) {
+            lo = min(lo, v[j]);
+            hi = max(hi, v[j]);
+            ++nz;
+        }
+    lo = lane63(wave_scan_dpp(lo, MinOp{}));
+    hi = lane63(wave_scan_dpp(hi, MaxOp{}));
+    nz = lane63(wave_scan_dpp(nz, AddOp{}));
+    if (lane == 0) {
+        rng[3 * wave] = lo;
+        rng[3 * wave + 1] = hi;
+        rng[3 * wave + 2] = nz;
+    }
+    __syncthreads();
+    lo = 0xffffffffu;
+    hi = 0u;
+    nz = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        lo = min(lo, rng[3 * w]);
+        hi = max(hi, rng[3 * w + 1]);
+        nz += rng[3 * w + 2];
+    }
+    __syncthreads();  // (rng is reused by the next call)
+#pragma unroll
+    for (int j = 0; j < P; ++j) v[j] = v[j] != 0u ? v[j] - lo + 1u : 0u;
+    if (nz < need) {
+        *thr = 0u;
+        *r = need - nz;
+        return;
+    }
+    int shift = max(0, 32 - __clz(hi - lo + 1u) - 12);
+    for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (v[j] != 0u) atomicAdd(&hist[v[j] >> shift], 1u);
+    __syncthreads();
+    find_bin_dpp<TT>(hist, BINS, need, sh, res);
+    uint32_t prefix = res[0], in_bin = res[2];
+    need -= res[1];
+    while (shift > 0 && in_bin != need) {
+        const int d = min(10, shift);
+        for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            if (v[j] != 0u && (v[j] >> shift) == prefix)
+                atomicAdd(&hist[(v[j] >> (shift - d)) & ((1u << d) - 1u)], 1u);
+        __syncthreads();
+        find_bin_dpp<TT>(hist, 1024, need, sh, res);
+        prefix = (prefix << d) | res[0];
+        need -= res[1];
+        in_bin = res[2];
+        shift -= d;
+    }
+    *thr = shift == 0 ? prefix : max(prefix << shift, 1u);
+    *r = shift == 0 ? need : 0xffffffffu;
+}
+
+// Exact top-k of a row from its candidates (keys and token indices, any
+// order; every key >= the row's k-th key is among them), selected in
+// registers -- P candidates per thread: the k-th key and
+// the number of its ties to keep (kth_largest_rebased), among the ties the
+// lowest indices (the same selection on the inverted indices), then the picks
+// in ascending index order through a bitmap over windows of BM_BITS token
+// indices and a block scan of the per-thread bit counts.
+// key[j], cid[j]: the thread's candidates (cid -1: no candidate, key 0);
+// every key >= the row's k-th key is among them, and there are >= k.
+template <int P>
+__device__ void select_cands_reg(uint32_t (&key)[P], const int32_t (&cid)[P], int k, int n_cand,
+                                 int32_t* __restrict__ out, uint32_t* hist, uint32_t* sh, uint32_t* res,
+                                 uint32_t* rng) {
+    static_assert(BINS % TT == 0, "work per thread");
+    const int tid = threadIdx.x;
+    uint32_t inv[P];
+    // keys of 0 (NaN) may be candidates too: they are the lowest, and with
+    // >= k candidates kth_largest_rebased's "fewer than k" case leaves r
+    // ties among them
+    uint32_t kthr, r;
+    kth_largest_rebased<P>(key, (uint32_t)k, hist, sh, res, rng, &kthr, &r);
+    // ties of key kthr beyond the r to keep: the r lowest indices, i.e. the
+    // r largest inverted indices
+    uint32_t n_tie = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) n_tie += cid[j] >= 0 && key[j] == kthr;
+    n_tie = lane63(wave_scan_dpp(n_tie, AddOp{}));
+    if ((tid & 63) == 0) rng[tid >> 6] = n_tie;
+    __syncthreads();
+    n_tie = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n_tie += rng[w];
+    __syncthreads();
+    uint32_t ithr = 0u;  // ties kept: inverted (rebased) index >= ithr
+    const bool cut = r != 0xffffffffu && n_tie > r;
+#pragma unroll
+    for (int j = 0; j < P; ++j) inv[j] = cut && cid[j] >= 0 && key[j] == kthr ? ~(uint32_t)cid[j] : 0u;
+    if (cut) {
+        uint32_t r2;
+        kth_largest_rebased<P>(inv, r, hist, sh, res, rng, &ithr, &r2);
+    }
+    // emission in ascending index order
+    uint32_t emitted = 0;
+    for (int w0 = 0; w0 < n_cand; w0 += BM_BITS) {
+        for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const bool take = cid[j] >= 0 && (key[j] > kthr || (key[j] == kthr && (!cut || inv[j] >= ithr)));
+            const int e = cid[j] - w0;
+            if (take && e >= 0 && e < BM_BITS) atomicOr(&hist[e >> 5], 1u << (e & 31));
+        }
+        __syncthreads();
+        constexpr int WPT = BINS / TT;
+        uint32_t m[WPT], cnt = 0;
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            m[j] = hist[WPT * tid + j];
+            cnt += __popc(m[j]);
+        }
+        uint32_t total;
+        uint32_t p = emitted + block_scan_dpp<TT>(cnt, sh, &total);
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            uint32_t x = m[j];
+            while (x) {
+                const int b = __ffs(x) - 1;
+                x &= x - 1u;
+                out[p++] = w0 + 32 * (WPT * tid + j) + b;
+            }
+        }
+        emitted += total;
+    }
+}
+
 // One pass per row.  A threshold from a sample of the row (128 blocks of 16
 // consecutive scores spread over it) filters the keys while the row is read
 // once; each wave appends the keys at or above it to its own LDS region
 // (positions from a ballot, no atomics), the waves taking interleaved 64-key
 // blocks so that a dense stretch of high scores spreads over all of them.
 // The exact top-k is then selected among the candidates (all CAP1 slots; the
-// unused ones hold key 0).  A row whose sample
-// misleads (fewer than k candidates, or a wave region full) and short rows
-// take the two-pass selection instead.
+// unused ones hold key 0).  A row whose sample misleads (fewer than k
+// candidates, or a wave region full) takes the two-pass selection instead.
 constexpr int SAMP_BLOCKS = 128, SAMP_BLK = 16, SAMP = SAMP_BLOCKS * SAMP_BLK;
 constexpr int WREG = 384;              // candidate slots per wave
 constexpr int CAP1 = WREG * NW;        // 6144
@@ -168,87 +398,6 @@ __global__ __launch_bounds__(TT) void topk_rows(const float* __restrict__ scores
 // a CU and one row's loads overlap another row's LDS steps (WPE: the waves
 // per SIMD the register budget is cut for -- 8 for 256 threads x 32 keys,
 // 4 for 512 threads x 64 keys, i.e. eight and two rows per CU).
-
-// Inclusive scan over the 64 lanes of a wave with op (DPP: row_shr 1, 2, 4, 8
-// within rows of 16 lanes, then row_bcast 15 and 31 across rows).
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, Op op) {
-    const int lane = threadIdx.x & 63, rl = lane & 15;
-    uint32_t t;
-    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);
-    if (rl >= 1) v = op(v, t);
-    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);
-    if (rl >= 2) v = op(v, t);
-    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);
-    if (rl >= 4) v = op(v, t);
-    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);
-    if (rl >= 8) v = op(v, t);
-    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);
-    if ((lane & 31) >= 16) v = op(v, t);
-    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);
-    if (lane >= 32) v = op(v, t);
-    return v;
-}
-struct AddOp {
-    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
-};
-struct MinOp {
-    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
-};
-struct MaxOp {
-    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
-};
-__device__ __forceinline__ uint32_t lane63(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Exclusive prefix sum over the NTR threads in thread order; *total gets the
-// sum.  sh: NTR / 64 + 1 words.  Barriers inside: every thread calls it.
-template <int NTR>
-__device__ __forceinline__ uint32_t block_scan_dpp(uint32_t v, uint32_t* sh, uint32_t* total) {
-    constexpr int NWR = NTR / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t incl = wave_scan_dpp(v, AddOp{});
-    if (lane == 63) sh[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NWR; ++w) {
-        const uint32_t x = sh[w];
-        before += w < wave ? x : 0u;
-        all += x;
-    }
-    *total = all;
-    __syncthreads();
-    return before + incl - v;
-}
-
-// The bin of the need-th largest element over nb bins (read from the top):
-// (bin, count above it, count in it) into res.  Barriers inside.
-template <int NTR>
-__device__ __forceinline__ void find_bin_dpp(const uint32_t* hist, int nb, uint32_t need, uint32_t* sh,
-                                             uint32_t* res) {
-    const int per = nb / NTR;  // bins per thread: [hi - per, hi)
-    const int hi = nb - per * (int)threadIdx.x;
-    uint32_t cnt = 0;
-    for (int i = 1; i <= per; ++i) cnt += hist[hi - i];
-    uint32_t total;
-    const uint32_t above = block_scan_dpp<NTR>(cnt, sh, &total);
-    if (cnt > 0 && above < need && above + cnt >= need) {
-        uint32_t acc = above;
-        for (int i = 1; i <= per; ++i) {
-            const uint32_t h = hist[hi - i];
-            if (acc + h >= need) {
-                res[0] = (uint32_t)(hi - i);
-                res[1] = acc;
-                res[2] = h;
-                break;
-            }
-            acc += h;
-        }
-    }
-    __syncthreads();
-}
 
 template <int NTR, int PER, int WPE>
 __global__ __launch_bounds__(NTR, WPE) void topk_short_rows(const float* __restrict__ scores,
@@ -712,161 +861,6 @@ __device__ void rescore_row(const uint8_t* __restrict__ q, const float* __restri
     }
 }
 
-// The need-th largest of the values of v other than 0 (v: P per thread of a
-// TT-thread workgroup; 0 marks "not a value"), in registers.  The values are
-// rebased in place to v - lo + 1 (order kept, 0 stays 0; lo = the smallest
-// value) and *thr gets the need-th largest rebased value, *r how many values
-// equal to it to keep (0xffffffff: all of them; the bin they share is kept
-// whole).  With fewer than need values, *thr = 0 and *r = need - count (the
-// caller's 0 entries make up the rest).  hist: BINS words; sh: NW + 1;
-// res: 3; rng: 3 NW.  Barriers inside: every thread calls it.
-template <int P>
-__device__ void kth_largest_rebased(uint32_t (&v)[P], uint32_t need, uint32_t* hist, uint32_t* sh,
-                                    uint32_t* res, uint32_t* rng, uint32_t* thr, uint32_t* r) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t lo = 0xffffffffu, hi = 0u, nz = 0u;
-#pragma unroll
-    for (int j = 0; j < P; ++j)
-        if (v[j] != 0u) {
-            lo = min(lo, v[j]);
-            hi = max(hi, v[j]);
-            ++nz;
-        }
-    lo = lane63(wave_scan_dpp(lo, MinOp{}));
-    hi = lane63(wave_scan_dpp(hi, MaxOp{}));
-    nz = lane63(wave_scan_dpp(nz, AddOp{}));
-    if (lane == 0) {
-        rng[3 * wave] = lo;
-        rng[3 * wave + 1] = hi;
-        rng[3 * wave + 2] = nz;
-    }
-    __syncthreads();
-    lo = 0xffffffffu;
-    hi = 0u;
-    nz = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        lo = min(lo, rng[3 * w]);
-        hi = max(hi, rng[3 * w + 1]);
-        nz += rng[3 * w + 2];
-    }
-    __syncthreads();  // (rng is reused by the next call)
-#pragma unroll
-    for (int j = 0; j < P; ++j) v[j] = v[j] != 0u ? v[j] - lo + 1u : 0u;
-    if (nz < need) {
-        *thr = 0u;
-        *r = need - nz;
-        return;
-    }
-    int shift = max(0, 32 - __clz(hi - lo + 1u) - 12);
-    for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < P; ++j)
-        if (v[j] != 0u) atomicAdd(&hist[v[j] >> shift], 1u);
-    __syncthreads();
-    find_bin_dpp<TT>(hist, BINS, need, sh, res);
-    uint32_t prefix = res[0], in_bin = res[2];
-    need -= res[1];
-    while (shift > 0 && in_bin != need) {
-        const int d = min(10, shift);
-        for (int i = tid; i < 1024; i += TT) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < P; ++j)
-            if (v[j] != 0u && (v[j] >> shift) == prefix)
-                atomicAdd(&hist[(v[j] >> (shift - d)) & ((1u << d) - 1u)], 1u);
-        __syncthreads();
-        find_bin_dpp<TT>(hist, 1024, need, sh, res);
-        prefix = (prefix << d) | res[0];
-        need -= res[1];
-        in_bin = res[2];
-        shift -= d;
-    }
-    *thr = shift == 0 ? prefix : max(prefix << shift, 1u);
-    *r = shift == 0 ? need : 0xffffffffu;
-}
-
-// Exact top-k of a row from its candidate list (n_c >= k keys and token
-// indices in the workspace, any order; every key >= the row's k-th key is in
-// it), selected in registers -- 12 candidates per thread: the k-th key and
-// the number of its ties to keep (kth_largest_rebased), among the ties the
-// lowest indices (the same selection on the inverted indices), then the picks
-// in ascending index order through a bitmap over windows of BM_BITS token
-// indices and a block scan of the per-thread bit counts.
-__device__ void select_cands_reg(const uint32_t* __restrict__ wr, int n_c, int k, int n_cand,
-                                 int32_t* __restrict__ out, uint32_t* hist, uint32_t* sh, uint32_t* res,
-                                 uint32_t* rng) {
-    constexpr int P = CAPG / TT;
-    static_assert(CAPG % TT == 0 && BINS % TT == 0, "work per thread");
-    const int tid = threadIdx.x;
-    uint32_t key[P], inv[P];
-    int32_t cid[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        const int i = tid + j * TT;
-        key[j] = i < n_c ? wr[WS_CKEY + i] : 0u;
-        cid[j] = i < n_c ? (int32_t)wr[WS_CIDX + i] : -1;
-    }
-    // keys of 0 (NaN) are candidates too: they are the lowest, and the caller
-    // checked n_c >= k, so kth_largest_rebased's "fewer than k" case leaves
-    // r ties among them
-    uint32_t kthr, r;
-    kth_largest_rebased<P>(key, (uint32_t)k, hist, sh, res, rng, &kthr, &r);
-    // ties of key kthr beyond the r to keep: the r lowest indices, i.e. the
-    // r largest inverted indices
-    uint32_t n_tie = 0;
-#pragma unroll
-    for (int j = 0; j < P; ++j) n_tie += cid[j] >= 0 && key[j] == kthr;
-    n_tie = lane63(wave_scan_dpp(n_tie, AddOp{}));
-    if ((tid & 63) == 0) rng[tid >> 6] = n_tie;
-    __syncthreads();
-    n_tie = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) n_tie += rng[w];
-    __syncthreads();
-    uint32_t ithr = 0u;  // ties kept: inverted (rebased) index >= ithr
-    const bool cut = r != 0xffffffffu && n_tie > r;
-#pragma unroll
-    for (int j = 0; j < P; ++j) inv[j] = cut && cid[j] >= 0 && key[j] == kthr ? ~(uint32_t)cid[j] : 0u;
-    if (cut) {
-        uint32_t r2;
-        kth_largest_rebased<P>(inv, r, hist, sh, res, rng, &ithr, &r2);
-    }
-    // emission in ascending index order
-    uint32_t emitted = 0;
-    for (int w0 = 0; w0 < n_cand; w0 += BM_BITS) {
-        for (int i = tid; i < BINS; i += TT) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const bool take = cid[j] >= 0 && (key[j] > kthr || (key[j] == kthr && (!cut || inv[j] >= ithr)));
-            const int e = cid[j] - w0;
-            if (take && e >= 0 && e < BM_BITS) atomicOr(&hist[e >> 5], 1u << (e & 31));
-        }
-        __syncthreads();
-        constexpr int WPT = BINS / TT;
-        uint32_t m[WPT], cnt = 0;
-#pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-            m[j] = hist[WPT * tid + j];
-            cnt += __popc(m[j]);
-        }
-        uint32_t total;
-        uint32_t p = emitted + block_scan_dpp<TT>(cnt, sh, &total);
-#pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-            uint32_t x = m[j];
-            while (x) {
-                const int b = __ffs(x) - 1;
-                x &= x - 1u;
-                out[p++] = w0 + 32 * (WPT * tid + j) + b;
-            }
-        }
-        emitted += total;
-    }
-}
-
 __global__ __launch_bounds__(TT) void topk_cand_select(
     const uint8_t* __restrict__ q, const float* __restrict__ qs, const uint8_t* __restrict__ kk,
     const float* __restrict__ ks, const float* __restrict__ w, float* __restrict__ scores,
@@ -894,7 +888,17 @@ __global__ __launch_bounds__(TT) void topk_cand_select(
     uint32_t* sh = hist + BINS;      // NW + 1
     uint32_t* res = sh + NW + 1;     // 3
     uint32_t* rng = res + 3;         // 3 NW
-    select_cands_reg(wr, n_c, k, n_cand, out, hist, sh, res, rng);
+    constexpr int P = CAPG / TT;
+    static_assert(CAPG % TT == 0, "candidates per thread");
+    uint32_t key[P];
+    int32_t cid[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int i = tid + j * TT;
+        key[j] = i < n_c ? wr[WS_CKEY + i] : 0u;
+        cid[j] = i < n_c ? (int32_t)wr[WS_CIDX + i] : -1;
+    }
+    select_cands_reg<P>(key, cid, k, n_cand, out, hist, sh, res, rng);
 }
 
 }  // namespace

@@ -17,13 +17,23 @@ constexpr int BINS = seg::kBins; // first digit: key bits 31..20
 constexpr int CAP = 4096;        // LDS candidate capacity (two workgroups per CU)
 constexpr int KMAX = seg::kMaxK;
 
+// Inclusive sum over the 64 lanes of a wave: DPP row_shr 1, 2, 4, 8 within
+// rows of 16 lanes, then row_bcast 15 and 31 across rows.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t n = __shfl_up(v, o, 64);
-        if (lane >= o) v += n;
-    }
+    const int lane = threadIdx.x & 63, rl = lane & 15;
+    uint32_t t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);
+    if (rl >= 1) v += t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);
+    if (rl >= 2) v += t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);
+    if (rl >= 4) v += t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);
+    if (rl >= 8) v += t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);
+    if ((lane & 31) >= 16) v += t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);
+    if (lane >= 32) v += t;
     return v;
 }
 
