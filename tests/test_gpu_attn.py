@@ -25,8 +25,9 @@ def _random_idx(B, T, N, k, rng, n_valid=None, junk=False):
     return idx
 
 
-def _run(wl, idx_np, seed, where):
+def _run(wl, idx_np, seed, where, scale=None):
     dev = gpu_device()
+    scale = wl.sm_scale if scale is None else scale
     inp = make_inputs(wl, seed=seed, device="cpu")
     q, kv = inp["q"].to(dev), inp["kv"].to(dev)
     print(f"[attn] {where}", flush=True)
@@ -36,13 +37,12 @@ def _run(wl, idx_np, seed, where):
     lse_g = Guarded((B, T, H), torch.float32, dev, float("nan"))
     need = dsa.workspace_size(dsa.OP_ATTN, B, T, wl.N, 1, H, wl.d_v, k) if 1 <= k <= 2048 else 0
     ws = poisoned_workspace(need, dev)
-    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx_np).to(dev), wl.d_v, wl.sm_scale,
+    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx_np).to(dev), wl.d_v, scale,
                                    out=out_g.view, lse=lse_g.view, workspace=ws.view)
     torch.cuda.synchronize()
     for name, buf in (("out", out_g), ("lse", lse_g), ("workspace", ws)):
         buf.check(f"{where} {name}")
-    ref_o, ref_l = oracle.sparse_mqa_attention(np64(inp["q"]), np64(inp["kv"]), idx_np, wl.d_v,
-                                               wl.sm_scale)
+    ref_o, ref_l = oracle.sparse_mqa_attention(np64(inp["q"]), np64(inp["kv"]), idx_np, wl.d_v, scale)
     bf16 = wl.dtype == "bf16"
     check_attention(np64(out), ref_o, bf16, where)
     check_lse(np64(lse), ref_l, bf16, where)
@@ -66,6 +66,9 @@ def test_f32_junk_indices():
     (2, 2, 2500, 2048),
     (1, 300, 4000, 256),    # one workgroup per row (>= 256 rows)
     (1, 5, 700, 100),       # k not a multiple of the tile
+    (1, 80, 3000, 2048),    # 64 to 255 rows: split, several splits per CU round
+    (2, 50, 2000, 300),
+    (1, 64, 900, 100),
 ])
 def test_bf16_random_sets(B, T, N, k):
     wl = WORKLOADS["prefill_8k"].with_(B=B, T=T, N=N, k=k)
@@ -85,15 +88,28 @@ def test_bf16_junk_and_empty_rows():
     idx = _random_idx(1, 300, 900, 64, rng, junk=True)
     idx[0, 7] = -1
     _run(wl, idx, 5, "bf16 junk/empty, unsplit")
+    wl = WORKLOADS["prefill_8k"].with_(B=1, T=70, N=900, k=512)
+    idx = _random_idx(1, 70, 900, 512, rng, junk=True)
+    idx[0, 9] = -1
+    _run(wl, idx, 6, "bf16 junk/empty, 70 rows")
 
 
-@pytest.mark.parametrize("T", [2, 300])
+@pytest.mark.parametrize("T", [3, 80, 300])
+def test_bf16_negative_scale(T):
+    """A negative softmax scale (the kernel copies that track max(-s)) on the
+    split path (3 and 80 rows) and the one-workgroup-per-row path."""
+    wl = WORKLOADS["prefill_8k"].with_(B=1, T=T, N=2500, k=2048 if T == 3 else 512)
+    rng = np.random.default_rng(31 + T)
+    _run(wl, _random_idx(1, T, wl.N, wl.k, rng), 7, f"bf16 negative scale T={T}", scale=-wl.sm_scale)
+
+
+@pytest.mark.parametrize("T", [2, 64, 300])
 def test_bf16_large_logit_gap_reruns_exactly(T):
     """A selected key in a late tile whose rope part is scaled x80 lifts some
     heads' logits far above the first tile's max (more than 2^64 in exp2
     terms); the kernel must notice and redo the pass with the exact max."""
     dev = gpu_device()
-    wl = WORKLOADS["prefill_8k"].with_(B=1, T=T, N=3000, k=2048 if T == 2 else 256)
+    wl = WORKLOADS["prefill_8k"].with_(B=1, T=T, N=3000, k=2048 if T <= 64 else 256)
     rng = np.random.default_rng(21)
     idx = _random_idx(1, T, wl.N, wl.k, rng)
     inp = make_inputs(wl, seed=8, device="cpu")
