@@ -6,33 +6,35 @@
 // rope) per selected token is shared by all 128 query heads, and the value
 // is its 512-wide latent part.
 //
-// bf16 path: one workgroup (4 waves, 32 heads each, one wave per SIMD) per
-// query token and slot range.  The selected latent rows are gathered 32 at a
-// time (a tile) straight into LDS with direct-to-LDS loads (global_load_lds;
-// no registers in flight) through a ring of four 36 KiB stages; the loads of
-// tile i+3 are issued between the key-product MFMAs of tile i.  Latent rows
-// are stored with their 16-byte chunks swizzled so that both the key-product
-// fragment reads and the transposed value reads are free of bank conflicts.
+// bf16 path: one workgroup (4 waves, one per SIMD) per query token and slot
+// range.  The selected latent rows are gathered 32 at a time (a tile)
+// straight into LDS with direct-to-LDS loads (no registers in flight)
+// through a ring of four 36 KiB stages; the loads of tile i+2 are issued
+// between the key-product MFMAs of tile i.  Latent rows are stored with
+// their 16-byte chunks swizzled so that both the key-product fragment reads
+// and the transposed value reads are free of bank conflicts.
 //
-// Per wave and tile:
-//   S^T[key, head] = K[key, :] . Q[head, :]        18 x 4 bf16 MFMA 16x16x32
-//     (A = key rows from LDS, B = the wave's 32 query heads kept in VGPRs;
-//      S^T puts one head per lane column, the layout the P operand of the
-//      value product needs)
+// Per tile:
+//   S^T[key, head] = K[key, :] . Q[head, :]    wave w: heads 32w..32w+31,
+//     36 bf16 MFMA 32x32x16 in two accumulator chains (A = key rows from
+//     LDS, B = the wave's Q in VGPRs); S^T puts one head per lane column,
+//     the layout the P operand of the value product needs
 //   softmax in base 2 against a fixed reference max per head (the max of
 //     the first tile with a valid key): exp2(x - m_ref) may grow to
 //     2^REF_GAP, which fp32 sums and bf16 weights carry without loss of
 //     relative precision, so the accumulator is never rescaled; a tile that
 //     exceeds the reference by more than REF_GAP makes the workgroup redo
 //     the pass against the exact max it recorded
-//   O[head, v] += P[head, key] V[key, v]           2 x 32 bf16 MFMA 16x16x32
-//     (V^T fragments come from the latent rows in LDS through ds_read_b64_tr_b16
-//      transposed reads; the key order of the MFMA's K dimension matches the
-//      accumulator layout of S^T)
-// The O accumulator (32 heads x 512 fp32 per wave) lives in AGPRs.  Batches
-// with fewer rows than CUs split the slots over several workgroups; each
-// writes its O rows normalised in bf16 with its per-head (max, exp-sum), and
-// attn_combine merges them.
+//   P: each wave's 32 heads of weights (bf16) into a shared 8 KiB LDS buffer
+//   O[head, v] += P[head, key] V[key, v]      wave w: value columns
+//     128w..128w+127 of all 128 heads, 4 x 4 blocks x 2 k steps = 32 bf16
+//     MFMA 32x32x16 (V^T fragments from the latent rows in LDS through
+//     ds_read_b64_tr_b16 transposed reads; their key order matches the P
+//     operand's)
+// The O accumulator (128 heads x 128 fp32 columns per wave) lives in AGPRs.
+// Batches with fewer rows than CUs split the slots over several
+// workgroups; each writes its O rows normalised in bf16 with its per-head
+// (max, exp-sum), and attn_combine merges them.
 #include <type_traits>
 
 #include "attn_common.h"
