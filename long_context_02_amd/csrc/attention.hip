@@ -519,33 +519,44 @@ void sparse_mla_attn_bf16(
     if (hh == 0) s_l[h0 + hl] = l_tot;
     __syncthreads();
     // o[hb][cb] register i holds head 32hb + 8(i/4) + 4hh + i%4, column
-    // 128 wave + 32 cb + hl; normalise and stage the wave's 128 x 128 bf16
-    // block (32 KiB) in its own ring stage, then store it with 16-byte writes
-    uint16_t* ob = reinterpret_cast<uint16_t*>(ring + wave * STAGE);
+    // 128 wave + 32 cb + hl.  Normalised, rounded to bf16 and stored straight
+    // from registers in column pairs: adjacent lanes (hl even / odd) trade
+    // one value by DPP so that the even lane holds columns hl, hl+1 of head
+    // i and the odd lane columns hl-1, hl of head i+1; each store then writes
+    // four 64-byte row segments.
+    uint16_t* dst = PARTIAL ? part_o + (row * nsplit + split) * H * DV : out + row * H * DV;
+    const bool odd = (hl & 1) != 0;
+    // a buffer resource over the row's H x DV outputs: the lane's part of the
+    // byte offset in a VGPR, the head block / register / column block part a
+    // scalar constant per store
+    const auto o_rs = __builtin_amdgcn_make_buffer_rsrc(dst, 0, H * DV * 2, 0x00020000);
+    const int o_voff = ((4 * hh + (odd ? 1 : 0)) * DV + 128 * wave + (hl & ~1)) * 2;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const float4 lv = *reinterpret_cast<const float4*>(&s_l[32 * hb + 8 * i4 + 4 * hh]);
             const float la[4] = {lv.x, lv.y, lv.z, lv.w};
+            float inv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float inv = la[e] > 0.f ? 1.f / la[e] : 0.f;
-                const int head = 32 * hb + 8 * i4 + 4 * hh + e;
+            for (int e = 0; e < 4; ++e) inv[e] = la[e] > 0.f ? 1.f / la[e] : 0.f;
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    ob[head * 128 + 32 * cb + hl] = __builtin_bit_cast(uint16_t, (__bf16)(o[hb][cb][4 * i4 + e] * inv));
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const float x0 = o[hb][cb][4 * i4 + e] * inv[e];
+                    const float x1 = o[hb][cb][4 * i4 + e + 1] * inv[e + 1];
+                    const float send = odd ? x0 : x1;
+                    const float recv = __builtin_bit_cast(
+                        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xf, 0xf, false));
+                    const float lo = odd ? recv : x0, hi = odd ? x1 : recv;
+                    const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+                    __builtin_amdgcn_raw_buffer_store_b32(pk, o_rs, o_voff,
+                                                          ((32 * hb + 8 * i4 + e) * DV + 32 * cb) * 2, 0);
+                }
             }
         }
-    }
-    __syncthreads();
-    uint16_t* dst = PARTIAL ? part_o + (row * nsplit + split) * H * DV : out + row * H * DV;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        const int c = r * 64 + lane;  // 16-byte chunk of the wave's block: head c/16, piece c%16
-        const int head = c >> 4, piece = c & 15;
-        *reinterpret_cast<uint4*>(dst + head * DV + 128 * wave + 8 * piece) =
-            *reinterpret_cast<const uint4*>(ob + head * 128 + 8 * piece);
     }
 }
 
