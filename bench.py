@@ -552,8 +552,10 @@ def time_attn_mha(wl, g, idx, steps, stream, seed=0):
     the per-head keys and values of every latent row are up-projected, then
     each head attends over its own rows.  Algorithmic work: the up-projection
     (2 x 512 x 256 FLOP per latent row and head, the latent rows read, the
-    per-head rows written) and, per (query, selected token, head), a 192-wide
-    key and a 128-wide value gathered (640 bytes) for 2 x 320 FLOP."""
+    per-head rows written) and, per (query, selected token, head), the
+    head's 128-wide key part and 128-wide value gathered (512 bytes) for
+    2 x 320 FLOP, plus per (query, selected token) the 64-wide rope key part
+    that every head shares (128 bytes)."""
     dev = g["q"].device
     extra = make_mha_inputs(wl, seed=seed, device=dev)
     B, T, N, H = wl.B, wl.T, wl.N, wl.H
@@ -570,8 +572,8 @@ def time_attn_mha(wl, g, idx, steps, stream, seed=0):
     kt = dsa.kernel_times(fn)
     n_valid = int(((idx >= 0) & (idx < N)).sum().item())
     up_flop = 2.0 * 512 * 256 * H * B * N
-    up_bytes = B * N * (1152 + H * (192 + 128) * 2)
-    gather_bytes = n_valid * H * (192 + 128) * 2
+    up_bytes = B * N * (1152 + H * (128 + 128) * 2)
+    gather_bytes = n_valid * (H * (128 + 128) * 2 + 64 * 2)
     res = {"ms": round(ms, 4), "rows": B * T, "kernels": {}}
     for name, (_, t) in kt.items():
         if name == "mha_up_project":

@@ -226,10 +226,12 @@ DSA_API dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const 
  *  out  [B,T,H,d_vh]    bf16  fully overwritten
  *  lse  [B,T,H] f32 or NULL
  * Supported: H = 128, d_c = 512, d_r = 64, d_n = 128, d_vh = 128, bf16.
- * The up-projected keys and values of every latent row of the batch are
- * computed first (bf16 MFMA, fp32 accumulation, rounded to bf16) into the
- * workspace (dsa_workspace_size(DSA_OP_ATTN_MHA, B, T, N, 1, H, d_vh, k)
- * bytes = B*N*H*(192 + 128)*2 rounded up, 16-byte aligned, overwritten);
+ * The head-dependent parts of every latent row's keys and values
+ * (W_UK[h] c_s[:d_c], W_UV[h] c_s[:d_c]) are computed first (bf16 MFMA, fp32
+ * accumulation, rounded to bf16) into the workspace
+ * (dsa_workspace_size(DSA_OP_ATTN_MHA, B, T, N, 1, H, d_vh, k) bytes =
+ * B*N*H*(128 + 128)*2 rounded up, 16-byte aligned, overwritten); the rope
+ * part of the key, shared by all heads, is read from kv;
  * logits, softmax and accumulation are fp32, the output is rounded to bf16.
  * The call suits prefill-sized caches: a decode batch would up-project every
  * cached row of every sequence.

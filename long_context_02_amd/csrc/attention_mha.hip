@@ -11,19 +11,22 @@
 // with per-head queries [q_nope ; q_rope] (192).
 //
 // Two kernels:
-//  * mha_up_project: the per-head keys and values of every latent row into
-//    the workspace (bf16, fp32 accumulation), a dense contraction on bf16
-//    MFMA: out^T[col, token] = W[col, :] . c[token, :512] for the 256 output
-//    columns (128 key + 128 value) of one head and 64 tokens per workgroup;
-//    the rope part of the key is copied.
+//  * mha_up_project: the per-head key and value parts that depend on the head
+//    (W_UK[h] c_s[:512], W_UV[h] c_s[:512]) of every latent row into the
+//    workspace (bf16, fp32 accumulation), a dense contraction on bf16 MFMA:
+//    out^T[col, token] = W[col, :] . c[token, :512] for the 256 output
+//    columns (128 key + 128 value) of one head and 64 tokens per workgroup.
+//    The rope part of the key is one part shared by every head: it is read
+//    from the latent row itself.
 //  * sparse_mha_attn: one workgroup per query token, 16 waves x 8 heads, 8
-//    lanes per head.  Each selected token's key block ([128 heads][192],
-//    48 KiB) and value block ([128][128], 32 KiB) are contiguous, so a wave
-//    reads 3 KiB + 2 KiB per token in 16-byte pieces; a head's dot product
-//    is split over its 8 lanes (24 key dims each) and reduced across them.
-//    Online softmax in base 2 per head, fp32 accumulators, bf16 output.
-//    Every gathered key and value element is used once (no head shares it),
-//    so the kernel is bound by memory, not by arithmetic.
+//    lanes per head.  Each selected token's key block ([128 heads][128],
+//    32 KiB) and value block ([128][128], 32 KiB) are contiguous, so a wave
+//    reads 2 KiB + 2 KiB per token in 16-byte pieces, plus the token's
+//    128-byte rope part, which all heads read; a head's dot product is split
+//    over its 8 lanes (16 head key dims and 8 rope dims each) and reduced
+//    across them.  Online softmax in base 2 per head, fp32 accumulators, bf16
+//    output.  Every gathered per-head element is used once (no head shares
+//    it), so the kernel is bound by memory, not by arithmetic.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -120,20 +123,10 @@ __global__ __launch_bounds__(256) void mha_up_project(const uint16_t* __restrict
         const long long r = r0 + tok;
         if (r < rows) {
             const uint4 x = *reinterpret_cast<const uint4*>(st + tok * UP_PITCH + 8 * pc);
-            uint16_t* dst = wave < 2 ? kh + ((size_t)r * H + h) * DK + col0 + 8 * pc
+            uint16_t* dst = wave < 2 ? kh + ((size_t)r * H + h) * DN + col0 + 8 * pc
                                      : vh + ((size_t)r * H + h) * DVH + col0 + 8 * pc;
             *reinterpret_cast<uint4*>(dst) = x;
         }
-    }
-    // the rope part of the key: 64 rows x 128 bytes, copied
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int c = it * 256 + tid;
-        const int tok = c >> 3, pc = c & 7;
-        const long long r = r0 + tok;
-        if (r < rows)
-            *reinterpret_cast<uint4*>(kh + ((size_t)r * H + h) * DK + DN + 8 * pc) =
-                *reinterpret_cast<const uint4*>(kv + (size_t)r * LAT_ROW + DC + 8 * pc);
     }
 }
 
@@ -153,9 +146,9 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4& x, float* f) {
 }
 
 __global__ __launch_bounds__(AT) void sparse_mha_attn(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int T, int N,
-    int k, float scale_log2) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ kh,
+    const uint16_t* __restrict__ vh, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
+    float* __restrict__ lse, int T, int N, int k, float scale_log2) {
     __shared__ int32_t sidx[SLOTS];
     __shared__ int s_n;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -191,16 +184,19 @@ __global__ __launch_bounds__(AT) void sparse_mha_attn(
     __syncthreads();
     const int n = s_n;
 
-    // this lane's 24 query dims of head h
+    // this lane's 24 query dims of head h: head key dims 16p .. 16p+15 and
+    // rope dims 8p .. 8p+7
     float qf[24];
     {
-        const uint16_t* qp = q + (row * H + h) * DK + 24 * p;
+        const uint16_t* qp = q + (row * H + h) * DK;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) bf16x8_to_f32(*reinterpret_cast<const uint4*>(qp + 8 * j), qf + 8 * j);
+        for (int j = 0; j < 2; ++j) bf16x8_to_f32(*reinterpret_cast<const uint4*>(qp + 16 * p + 8 * j), qf + 8 * j);
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(qp + DN + 8 * p), qf + 16);
     }
-    const uint16_t* kb = kh + ((size_t)b * N * H + h) * DK + 24 * p;
+    const uint16_t* kb = kh + ((size_t)b * N * H + h) * DN + 16 * p;
+    const uint16_t* rb = kv + (size_t)b * N * LAT_ROW + DC + 8 * p;
     const uint16_t* vb = vh + ((size_t)b * N * H + h) * DVH + 16 * p;
-    const size_t kstride = (size_t)H * DK, vstride = (size_t)H * DVH;
+    const size_t kstride = (size_t)H * DN, vstride = (size_t)H * DVH;
 
     float o[16];
 #pragma unroll
@@ -217,7 +213,8 @@ __global__ __launch_bounds__(AT) void sparse_mha_attn(
             const uint16_t* kp = kb + (size_t)s * kstride;
             const uint16_t* vp = vb + (size_t)s * vstride;
 #pragma unroll
-            for (int c = 0; c < 3; ++c) kx[j][c] = *reinterpret_cast<const uint4*>(kp + 8 * c);
+            for (int c = 0; c < 2; ++c) kx[j][c] = *reinterpret_cast<const uint4*>(kp + 8 * c);
+            kx[j][2] = *reinterpret_cast<const uint4*>(rb + (size_t)s * LAT_ROW);
 #pragma unroll
             for (int c = 0; c < 2; ++c) vx[j][c] = *reinterpret_cast<const uint4*>(vp + 8 * c);
         }
@@ -273,7 +270,7 @@ __global__ __launch_bounds__(AT) void sparse_mha_attn(
 
 size_t attn_mha_workspace_bytes(int B, int N) {
     const size_t rows = (size_t)B * N;
-    return align_up(rows * H * DK * sizeof(uint16_t)) + align_up(rows * H * DVH * sizeof(uint16_t));
+    return align_up(rows * H * DN * sizeof(uint16_t)) + align_up(rows * H * DVH * sizeof(uint16_t));
 }
 
 dsa_status launch_attn_mha_bf16(const void* q, const void* kv, const void* w_uk, const void* w_uv,
@@ -286,7 +283,7 @@ dsa_status launch_attn_mha_bf16(const void* q, const void* kv, const void* w_uk,
         return DSA_ERR_UNSUPPORTED;
     auto* kh = static_cast<uint16_t*>(workspace);
     auto* vh = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
-                                           align_up((size_t)rows_kv * H * DK * sizeof(uint16_t)));
+                                           align_up((size_t)rows_kv * H * DN * sizeof(uint16_t)));
     DSA_TIMED("mha_up_project", stream,
               mha_up_project<<<dim3((unsigned)((rows_kv + UP_ROWS - 1) / UP_ROWS), H), 256, 0,
                                stream>>>(static_cast<const uint16_t*>(kv),
@@ -296,8 +293,8 @@ dsa_status launch_attn_mha_bf16(const void* q, const void* kv, const void* w_uk,
     if (st != DSA_OK) return st;
     DSA_TIMED("sparse_mha_attn", stream,
               sparse_mha_attn<<<dim3((unsigned)rows_q), AT, 0, stream>>>(
-                  static_cast<const uint16_t*>(q), kh, vh, idx, static_cast<uint16_t*>(out), lse, T,
-                  N, k, sm_scale * kLog2e));
+                  static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), kh, vh, idx,
+                  static_cast<uint16_t*>(out), lse, T, N, k, sm_scale * kLog2e));
     return launch_status();
 }
 

@@ -240,7 +240,7 @@ def test_forward_noalloc_rejects_before_launching():
 def test_attention_mha_rejects_bad_arguments():
     f = dsa.lib().dsa_sparse_mla_attn_mha
     need = dsa.workspace_size(dsa.OP_ATTN_MHA, 1, 4, 10, 8, 128, 128, 64)
-    assert need >= 10 * 128 * (192 + 128) * 2
+    assert need >= 10 * 128 * (128 + 128) * 2
     with pytest.raises(ValueError):
         dsa.workspace_size(dsa.OP_ATTN_MHA, 1, 4, 10, 8, 64, 128, 64)
 
