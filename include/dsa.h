@@ -230,8 +230,11 @@ DSA_API dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const 
  * (W_UK[h] c_s[:d_c], W_UV[h] c_s[:d_c]) are computed first (bf16 MFMA, fp32
  * accumulation, rounded to bf16) into the workspace
  * (dsa_workspace_size(DSA_OP_ATTN_MHA, B, T, N, 1, H, d_vh, k) bytes =
- * B*N*H*(128 + 128)*2 rounded up, 16-byte aligned, overwritten); the rope
- * part of the key, shared by all heads, is read from kv;
+ * B*N*H*(128 + 128)*2 rounded up, 16-byte aligned, overwritten; after the
+ * call it holds the key parts as [B*N][H][d_n] bf16 from byte 0 and the
+ * value parts as [B*N][H][d_vh] bf16 from byte B*N*H*d_n*2 rounded up to a
+ * multiple of 256); the rope part of the key, shared by all heads, is read
+ * from kv;
  * logits, softmax and accumulation are fp32, the output is rounded to bf16.
  * The call suits prefill-sized caches: a decode batch would up-project every
  * cached row of every sequence.

@@ -14,8 +14,8 @@
 //  * mha_up_project: the per-head key and value parts that depend on the head
 //    (W_UK[h] c_s[:512], W_UV[h] c_s[:512]) of every latent row into the
 //    workspace (bf16, fp32 accumulation), a dense contraction on bf16 MFMA:
-//    out^T[col, token] = W[col, :] . c[token, :512] for the 256 output
-//    columns (128 key + 128 value) of one head and 64 tokens per workgroup.
+//    out[token, col] = c[token, :512] . W[col, :] for the 256 output
+//    columns (128 key + 128 value) of one head and 128 tokens per workgroup.
 //    The rope part of the key is one part shared by every head: it is read
 //    from the latent row itself.
 //  * sparse_mha_attn: one workgroup per query token, 16 waves x 8 heads, 8
@@ -47,87 +47,175 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Up-projection: 256 threads, 64 latent rows x (one head's 256 output columns).
-// Wave w: columns 64*(w&1) .. +63 of the key part (w < 2, W = W_UK[h]) or of
-// the value part (w >= 2, W = W_UV[h]).  Per 32-wide k step a wave does 4 x 4
-// MFMAs (column blocks x token blocks) on fragments loaded from global memory
-// (the 64 rows' latent tile is shared by the four waves through the caches).
-constexpr int UP_ROWS = 64;
-constexpr int UP_PITCH = 64 + 8;  // LDS staging row: 64 bf16 + 16 bytes pad
+// Up-projection: out[row, col] = c[row, :512] . W[col, :] for the 256 output
+// columns of one head (W_UK[h]'s 128 rows, then W_UV[h]'s) and 128 latent rows
+// per workgroup (4 waves: wave w takes rows 64 (w / 2) .. +63 and the key
+// (w even) or value (w odd) columns; 2 x 4 blocks of 32 x 32 fp32 per wave).
+// The contraction runs in 16 chunks of 32 k: each chunk's 128 latent rows
+// and 256 weight rows (64 bytes each) are staged in LDS, double-buffered,
+// and its global loads are issued two chunks ahead of its product (two
+// register sets), so two chunks' MFMA work covers their latency; two
+// workgroups share a CU (48 KiB of LDS each).  A row's four 16-byte pieces
+// sit at slot q ^ ((r / 4) % 4), so the 16 lanes that read one piece of 16
+// consecutive rows hit distinct banks.
+// bf16 v_mfma_f32_32x32x16: A = 16 bytes of a latent row, B = 16 bytes of a
+// weight row (both k-contiguous).  Results go out in bf16 straight from the
+// accumulators, adjacent lanes pairing columns by DPP (4-byte streaming
+// stores: the 8 GiB of per-head rows would only evict the latent rows and
+// weights from the caches).
+// Workgroup order: workgroups are handed to the 8 XCDs in turn, so XCD x
+// takes row blocks x, x + 8, ...; along one XCD the head runs fastest within
+// a group of UP_HG heads, so the workgroups resident on an XCD at once share
+// latent row blocks through its L2 while the group's weights stay there too.
+constexpr int UP_ROWS = 128;          // latent rows per workgroup
+constexpr int UP_HG = 8;              // heads per group (grid y = H / UP_HG)
+static_assert(H % UP_HG == 0, "head groups must tile the heads");
+constexpr int UP_COLS = 2 * DN;       // output columns per workgroup (one head: key + value)
+constexpr int UP_BK = 32;             // k per chunk
+constexpr int UP_A = UP_ROWS * UP_BK; // bf16 per A chunk
+constexpr int UP_B = UP_COLS * UP_BK; // bf16 per B chunk
 
-__global__ __launch_bounds__(256) void mha_up_project(const uint16_t* __restrict__ kv,
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBuf = 0x00020000;  // buffer resource word 3: raw (untyped) 32-bit data
+
+__device__ __forceinline__ int up_slot(int r, int q) { return 4 * r + (q ^ ((r >> 2) & 3)); }
+
+__global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restrict__ kv,
                                                       const uint16_t* __restrict__ w_uk,
                                                       const uint16_t* __restrict__ w_uv,
                                                       uint16_t* __restrict__ kh,
                                                       uint16_t* __restrict__ vh, long long rows) {
-    __shared__ __attribute__((aligned(16))) uint16_t stage[4][UP_ROWS * UP_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][UP_A];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][UP_B];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int m = lane & 15, g = lane >> 4;
-    const int h = blockIdx.y;
-    const long long r0 = (long long)blockIdx.x * UP_ROWS;
-    const uint16_t* __restrict__ W = (wave < 2 ? w_uk : w_uv) + (size_t)h * 128 * DC;
-    const int col0 = 64 * (wave & 1);
+    const int s_x = blockIdx.x >> 3;  // position along XCD blockIdx.x % 8
+    const int h = blockIdx.y * UP_HG + s_x % UP_HG;
+    const long long r0 = ((long long)(s_x / UP_HG) * 8 + (blockIdx.x & 7)) * UP_ROWS;
+    if (r0 >= rows) return;
+    const int wr = wave >> 1, wc = wave & 1;  // row half, key / value columns
+    const int i32 = lane & 31, half = lane >> 5;
 
-    f32x4 acc[4][4];
+    // chunk loads through buffer resources: A = 128 latent rows x 4 pieces
+    // (2 per thread), B = 256 weight rows x 4 pieces (4 per thread); thread
+    // tid moves piece tid % 4 of rows tid / 4 + 64 j.  Latent rows past the
+    // end read as zeros (every offset sits in the range-checked vector offset).
+    const int nrow = (int)(rows - r0 < UP_ROWS ? rows - r0 : UP_ROWS);
+    const auto a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kv + (size_t)r0 * LAT_ROW), 0,
+                                                        nrow * LAT_ROW * 2, kRawBuf);
+    const auto k_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w_uk + (size_t)h * DN * DC), 0,
+                                                        DN * DC * 2, kRawBuf);
+    const auto v_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w_uv + (size_t)h * DVH * DC), 0,
+                                                        DVH * DC * 2, kRawBuf);
+    const int pr = tid >> 2, pq = tid & 3;
+    const int a_voff = pr * LAT_ROW * 2 + 16 * pq;
+    const int b_voff = pr * DC * 2 + 16 * pq;
+    const int st_el = 8 * up_slot(pr, pq);  // + 64 rows = + 4096 bytes (the slot swizzle repeats)
+    struct Chunk { u32x4 a[2], b[4]; };
+    auto load = [&](Chunk& c, int kc) __attribute__((always_inline)) {
+        const int ko = UP_BK * 2 * kc;
+        c.a[0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff + ko, 0, 0);
+        c.a[1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff + 64 * LAT_ROW * 2 + ko, 0, 0);
+        c.b[0] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, b_voff + ko, 0, 0);
+        c.b[1] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, b_voff + 64 * DC * 2 + ko, 0, 0);
+        c.b[2] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, b_voff + ko, 0, 0);
+        c.b[3] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, b_voff + 64 * DC * 2 + ko, 0, 0);
+    };
+    auto stage = [&](const Chunk& c, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&lds_a[buf][st_el + 2048 * j]) = c.a[j];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&lds_b[buf][st_el + 2048 * j]) = c.b[j];
+    };
 
-    // this lane's rows: weights row col0 + 16 cb + m, latent rows r0 + 16 tb + m
-    const uint16_t* wrow[4];
+    f32x16_t acc[2][4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) wrow[cb] = W + (size_t)(col0 + 16 * cb + m) * DC + 8 * g;
-    const uint16_t* crow[4];
-    bool cvalid[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const long long r = r0 + 16 * tb + m;
-        cvalid[tb] = r < rows;
-        crow[tb] = kv + (size_t)(cvalid[tb] ? r : 0) * LAT_ROW + 8 * g;
-    }
-#pragma unroll 2
-    for (int ks = 0; ks < DC / 32; ++ks) {
-        bf16x8_t a[4], b[4];
+    for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
-            a[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wrow[cb] + 32 * ks));
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            uint4 x = *reinterpret_cast<const uint4*>(crow[tb] + 32 * ks);
-            if (!cvalid[tb]) x = uint4{0u, 0u, 0u, 0u};
-            b[tb] = __builtin_bit_cast(bf16x8_t, x);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma16(a[cb], b[tb], acc[cb][tb]);
-    }
+            for (int e = 0; e < 16; ++e) acc[rb2][cb][e] = 0.f;
 
-    // acc[cb][tb] lane (m, g): out^T[col 16cb + 4g + i][token 16tb + m].
-    // Stage as [token][64 columns] bf16, then store 16-byte row pieces.
-    uint16_t* st = stage[wave];
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+        for (int ks = 0; ks < UP_BK / 16; ++ks) {
+            // k step ks: piece 2 ks + half of each row
+            bf16x8_t af[2], bf[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const uint32_t lo = (uint32_t)bf16_bits(acc[cb][tb][0]) | ((uint32_t)bf16_bits(acc[cb][tb][1]) << 16);
-            const uint32_t hi = (uint32_t)bf16_bits(acc[cb][tb][2]) | ((uint32_t)bf16_bits(acc[cb][tb][3]) << 16);
-            *reinterpret_cast<uint2*>(st + (16 * tb + m) * UP_PITCH + 16 * cb + 4 * g) = uint2{lo, hi};
+            for (int rb2 = 0; rb2 < 2; ++rb2)
+                af[rb2] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                    &lds_a[buf][8 * up_slot(64 * wr + 32 * rb2 + i32, 2 * ks + half)]));
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                bf[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(
+                    &lds_b[buf][8 * up_slot(128 * wc + 32 * cb + i32, 2 * ks + half)]));
+#pragma unroll
+            for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[rb2][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb2], bf[cb], acc[rb2][cb], 0, 0, 0);
         }
+    };
+
+    // Chunk kc is multiplied from LDS buffer kc % 2; chunk kc + 1 waits in
+    // register set (kc + 1) % 2 and chunk kc + 2 in set kc % 2, so a chunk's
+    // loads have two chunks' products to land.  After chunk kc's product,
+    // chunk kc + 1 goes to LDS buffer (kc + 1) % 2 (last read by chunk kc - 1,
+    // before the previous barrier) and its register set takes chunk kc + 3.
+    constexpr int NKC = DC / UP_BK;
+    static_assert(NKC % 2 == 0 && NKC >= 4, "chunk pipeline assumes an even chunk count");
+    // (scheduling barriers keep the loads where they are written: the
+    // compiler would otherwise sink them next to their first use)
+    Chunk c0, c1;
+    load(c0, 0);
+    load(c1, 1);
+    stage(c0, 0);
+    load(c0, 2);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int c = it * 64 + lane;  // 16-byte piece: token c / 8, columns 8 * (c % 8)
-        const int tok = c >> 3, pc = c & 7;
-        const long long r = r0 + tok;
-        if (r < rows) {
-            const uint4 x = *reinterpret_cast<const uint4*>(st + tok * UP_PITCH + 8 * pc);
-            uint16_t* dst = wave < 2 ? kh + ((size_t)r * H + h) * DN + col0 + 8 * pc
-                                     : vh + ((size_t)r * H + h) * DVH + col0 + 8 * pc;
-            *reinterpret_cast<uint4*>(dst) = x;
+    for (int kc = 0; kc < NKC; kc += 2) {
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        stage(c1, 1);
+        __syncthreads();
+        if (kc + 3 < NKC) load(c1, kc + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kc + 2 < NKC) {
+            stage(c0, 0);
+            __syncthreads();
+            if (kc + 4 < NKC) load(c0, kc + 4);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
+
+    // acc[rb2][cb] register e of lane (i32, half): row 64 wr + 32 rb2 + 8 (e / 4)
+    // + 4 half + e % 4, column 32 cb + i32 of the wave's 128.  Adjacent lanes
+    // (i32 even / odd) trade one value so that the even lane holds columns
+    // i32, i32 + 1 of row e and the odd lane columns i32 - 1, i32 of row e + 1.
+    const bool odd = (i32 & 1) != 0;
+    uint16_t* const base = wc == 0 ? kh : vh;
+#pragma unroll
+    for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float x0 = acc[rb2][cb][e], x1 = acc[rb2][cb][e + 1];
+                const float send = odd ? x0 : x1;
+                const float recv = __builtin_bit_cast(
+                    float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xf, 0xf, false));
+                const float lo = odd ? recv : x0, hi = odd ? x1 : recv;
+                const int r = 64 * wr + 32 * rb2 + 8 * (e >> 2) + 4 * half + (e & 3) + (odd ? 1 : 0);
+                const long long gr = r0 + r;
+                if (gr < rows) {
+                    const uint32_t pk = (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+                    __builtin_nontemporal_store(
+                        pk, reinterpret_cast<uint32_t*>(base + ((size_t)gr * H + h) * DN + 32 * cb + (i32 & ~1)));
+                }
+            }
 }
 
 // ---------------------------------------------------------------------------
@@ -279,13 +367,15 @@ dsa_status launch_attn_mha_bf16(const void* q, const void* kv, const void* w_uk,
     if (k > SLOTS) return DSA_ERR_UNSUPPORTED;
     const long long rows_kv = (long long)B * N;
     const long long rows_q = (long long)B * T;
-    if (rows_q > 0x7fffffffLL || (rows_kv + UP_ROWS - 1) / UP_ROWS > 0x7fffffffLL)
-        return DSA_ERR_UNSUPPORTED;
+    // up-projection grid: x = 8 XCDs x (row blocks per XCD) x UP_HG heads,
+    // 256 threads each; the x extent in threads must stay below 2^32
+    const long long up_jb = ((rows_kv + UP_ROWS - 1) / UP_ROWS + 7) / 8;
+    if (rows_q > 0x7fffffffLL || up_jb * 8 * UP_HG * 256 > 0xffffffffLL) return DSA_ERR_UNSUPPORTED;
     auto* kh = static_cast<uint16_t*>(workspace);
     auto* vh = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
                                            align_up((size_t)rows_kv * H * DN * sizeof(uint16_t)));
     DSA_TIMED("mha_up_project", stream,
-              mha_up_project<<<dim3((unsigned)((rows_kv + UP_ROWS - 1) / UP_ROWS), H), 256, 0,
+              mha_up_project<<<dim3((unsigned)(up_jb * 8 * UP_HG), H / UP_HG), 256, 0,
                                stream>>>(static_cast<const uint16_t*>(kv),
                                          static_cast<const uint16_t*>(w_uk),
                                          static_cast<const uint16_t*>(w_uv), kh, vh, rows_kv));

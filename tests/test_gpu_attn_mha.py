@@ -77,8 +77,42 @@ def test_small_batch_every_row():
     assert np.all(got_o[2] == 0) and np.all(np.isneginf(got_l[2]))
 
 
+@pytest.mark.parametrize("B,N", [(1, 130), (3, 77), (1, 128)])
+def test_up_projected_rows_in_workspace(B, N):
+    """The head-dependent key and value parts of every latent row, read back
+    from the workspace (layout as the header states), against the oracle's
+    float64 W_UK[h] c_s and W_UV[h] c_s: the kernel rounds fp32 sums to bf16,
+    so each element is within 2^-8 of its size plus the fp32 summation error
+    of 512 terms.  B*N = 130 leaves a 2-row tail after one 128-row block,
+    231 a 103-row tail; 128 is one whole block."""
+    dev = gpu_device()
+    wl = WORKLOADS["prefill_8k"].with_(B=B, T=1, N=N, k=16)
+    print(f"[mha] workspace rows B={B} N={N}", flush=True)
+    g = _inputs(wl, 23, dev)
+    idx_t = torch.zeros(B, 1, 16, dtype=torch.int32, device=dev)
+    rows, H = B * N, 128
+    need = dsa.workspace_size(dsa.OP_ATTN_MHA, B, 1, N, wl.H_I, H, 128, 16)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=dev)
+    dsa.sparse_mla_attn_mha(g["q_mha"], g["kv"], g["w_uk"], g["w_uv"], idx_t, g["sm_scale_mha"],
+                            workspace=ws)
+    torch.cuda.synchronize()
+    k_bytes = rows * H * 128 * 2
+    v_off = (k_bytes + 255) // 256 * 256
+    kh = np64(ws[:k_bytes].view(torch.bfloat16).reshape(rows, H, 128))
+    vh = np64(ws[v_off:v_off + k_bytes].view(torch.bfloat16).reshape(rows, H, 128))
+    K, V = oracle.mha_keys_values(np64(g["kv"]).reshape(rows, -1), np64(g["w_uk"]), np64(g["w_uv"]), D_C)
+    # nothing written outside the two arrays
+    pad = torch.cat([ws[k_bytes:v_off], ws[v_off + k_bytes:]]).cpu()
+    assert bool((pad == 0xAB).all())
+    for name, got, ref in (("key", kh, K[:, :, :128]), ("value", vh, V)):
+        err = np.abs(got - ref)
+        bound = np.abs(ref) * 2.0 ** -8 + 1e-3
+        bad = np.argwhere(err > bound)
+        assert bad.size == 0, f"{name}: {len(bad)} elements off, first {bad[:3].tolist()}"
+
+
 def test_ragged_up_projection_rows_and_two_sequences():
-    # B*N not a multiple of the 64-row up-projection tile
+    # B*N not a multiple of the 128-row up-projection tile
     dev = gpu_device()
     wl = WORKLOADS["prefill_8k"].with_(B=2, T=3, N=1001, k=2048)
     print("[mha] B=2 T=3 N=1001 k=2048", flush=True)
