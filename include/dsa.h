@@ -192,8 +192,9 @@ DSA_API dsa_status dsa_sparse_mla_attn(const void* q, const void* kv, const int3
  * scheduling, so the last bits of dkv vary from run to run.  Rows are
  * processed 2048 at a time; the workspace (dsa_workspace_size(
  * DSA_OP_ATTN_BWD, ...) bytes, 16-byte aligned, overwritten) holds one such
- * block's P and dS tiles, slot vectors and per-token lists, plus a count and
- * an offset per token of the batch (B*N of each).  attn_dtype must be DSA_BF16.
+ * block's P and dS tiles, slot vectors and per-token lists, a count and an
+ * offset per token of the batch (B*N of each) and the list of the tokens a
+ * block selects.  attn_dtype must be DSA_BF16.
  */
 DSA_API dsa_status dsa_sparse_mla_attn_bwd(const void* q, const void* kv, const int32_t* idx,
                                    const void* out, const float* lse, const void* dout,

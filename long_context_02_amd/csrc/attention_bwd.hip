@@ -520,7 +520,11 @@ __global__ __launch_bounds__(256) void zero_i32(int* __restrict__ p, size_t n) {
 // Sum of the contribution rows per token.  A pair p = lrow * k_pad + slot of
 // the block's rows selects token key = b * N + idx; the pairs of each token
 // are listed contiguously (counting sort: count with ranks, exclusive scan of
-// the counts, placement), then one wave per token adds its rows.
+// the counts, placement), then one wave per token adds its rows.  When the
+// batch has many more cache rows than a block has pairs (decode-shaped
+// batches), placement also lists the tokens that have pairs (the pair of rank
+// 0 appends its token; cnt[nkeys] counts them), so the sum runs over the
+// selected tokens only, not over every row of the cache.
 
 __global__ __launch_bounds__(256) void bwd_count(const int32_t* __restrict__ idx, int* __restrict__ cnt,
                                                 int* __restrict__ rank, long long row0, int rows, int T,
@@ -605,15 +609,29 @@ __global__ __launch_bounds__(256) void scan_apply(const int* __restrict__ cnt, c
 
 __global__ __launch_bounds__(256) void bwd_place(const int32_t* __restrict__ idx, const int* __restrict__ off,
                                                 const int* __restrict__ rank, int* __restrict__ list,
-                                                long long row0, int rows, int T, int N, int k, int k_pad) {
+                                                int* __restrict__ cnt, int* __restrict__ touched,
+                                                long long nkeys, long long row0, int rows, int T, int N,
+                                                int k, int k_pad) {
+    __shared__ int s_n, s_base;
     const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (p >= (long long)rows * k_pad) return;
-    const int r = rank[p];
-    if (r < 0) return;
-    const int lrow = (int)(p / k_pad), slot = (int)(p % k_pad);
-    const long long row = row0 + lrow;
-    const int id = idx[row * k + slot];
-    list[off[(row / T) * N + id] + r] = (int)p;
+    const int r = p < (long long)rows * k_pad ? rank[p] : -1;
+    long long key = 0;
+    if (r >= 0) {
+        const int lrow = (int)(p / k_pad), slot = (int)(p % k_pad);
+        const long long row = row0 + lrow;
+        const int id = idx[row * k + slot];
+        key = (row / T) * N + id;
+        list[off[key] + r] = (int)p;
+    }
+    if (!touched) return;
+    // the workgroup's first pairs append their tokens with one global atomic
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    const int loc = r == 0 ? atomicAdd(&s_n, 1) : 0;
+    __syncthreads();
+    if (threadIdx.x == 0 && s_n > 0) s_base = atomicAdd(&cnt[nkeys], s_n);
+    __syncthreads();
+    if (r == 0) touched[s_base + loc] = (int)key;
 }
 
 __device__ __forceinline__ void add_bf16x8(float* a, const uint4& x) {
@@ -625,15 +643,17 @@ __device__ __forceinline__ void add_bf16x8(float* a, const uint4& x) {
     }
 }
 
-// one wave per token: lane l adds 16-byte chunks l and (l < 8) l + 64 of the
-// token's contribution rows (72 chunks of 8 bf16), four rows per round, then
-// adds the sum to dkv (earlier blocks' sums are already there)
+// one wave per token (touched == NULL) or per listed token: lane l adds
+// 16-byte chunks l and (l < 8) l + 64 of the token's contribution rows (72
+// chunks of 8 bf16), four rows per round, then adds the sum to dkv (earlier
+// blocks' sums are already there)
 __global__ __launch_bounds__(256) void bwd_reduce(const uint16_t* __restrict__ contrib,
                                                  const int* __restrict__ cnt, const int* __restrict__ off,
-                                                 const int* __restrict__ list, float* __restrict__ dkv,
-                                                 long long nkeys) {
-    const long long key = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (key >= nkeys) return;
+                                                 const int* __restrict__ list, const int* __restrict__ touched,
+                                                 float* __restrict__ dkv, long long nkeys) {
+    const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= (touched ? (long long)cnt[nkeys] : nkeys)) return;
+    const long long key = touched ? (long long)touched[w] : w;
     const int n = cnt[key];
     if (n == 0) return;
     const int lane = threadIdx.x & 63;
@@ -677,7 +697,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(const uint16_t* __restrict__ c
 constexpr long long kBwdRows = 2048;
 
 struct BwdLayout {
-    size_t p, ds, contrib, rank, list, cnt, off, sums, total;
+    size_t p, ds, contrib, rank, list, cnt, off, sums, touched, total;
 };
 
 BwdLayout bwd_layout(long long rows, long long nkeys, int k) {
@@ -692,9 +712,10 @@ BwdLayout bwd_layout(long long rows, long long nkeys, int k) {
     L.contrib = take(pairs * DQK * sizeof(uint16_t));
     L.rank = take(pairs * sizeof(int));
     L.list = take(pairs * sizeof(int));
-    L.cnt = take((size_t)nkeys * sizeof(int));
+    L.cnt = take((size_t)(nkeys + 1) * sizeof(int));  // + the count of listed tokens
     L.off = take((size_t)nkeys * sizeof(int));
     L.sums = take((size_t)((nkeys + SCAN_CHUNK - 1) / SCAN_CHUNK) * sizeof(int));
+    L.touched = take((size_t)std::min<long long>(nkeys, (long long)pairs) * sizeof(int));  // listed tokens
     L.total = at;
     return L;
 }
@@ -724,6 +745,7 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
     int* cnt = reinterpret_cast<int*>(w + L.cnt);
     int* off = reinterpret_cast<int*>(w + L.off);
     int* sums = reinterpret_cast<int*>(w + L.sums);
+    int* touched = reinterpret_cast<int*>(w + L.touched);
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kk = static_cast<const uint16_t*>(kv);
     const auto* oo = static_cast<const uint16_t*>(out);
@@ -740,9 +762,10 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
         const int nr = (int)std::min<long long>(rb, rows - r0);
         const long long npairs = (long long)nr * k_pad;
         const unsigned gp = (unsigned)((npairs + 255) / 256);
+        const bool use_list = nkeys > 4 * npairs;  // most cache rows unselected
         DSA_TIMED("zero_i32", stream,
-                  zero_i32<<<dim3((unsigned)std::min<long long>((nkeys + 255) / 256, 8192)), 256, 0,
-                             stream>>>(cnt, (size_t)nkeys));
+                  zero_i32<<<dim3((unsigned)std::min<long long>((nkeys + 256) / 256, 8192)), 256, 0,
+                             stream>>>(cnt, (size_t)nkeys + 1));
         DSA_TIMED("sparse_mla_bwd_dq", stream,
                   sparse_mla_bwd_dq<<<dim3((unsigned)((nr + 7) / 8 * 16)), NT, 0, stream>>>(
                       qq, kk, idx, oo, lse, dd, dq, ws_p, ws_ds, r0, nr, T, N, k, ntile,
@@ -758,10 +781,14 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
         DSA_TIMED("scan_apply", stream,
                   scan_apply<<<dim3(nchunks), 256, 0, stream>>>(cnt, sums, off, nkeys));
         DSA_TIMED("bwd_place", stream,
-                  bwd_place<<<dim3(gp), 256, 0, stream>>>(idx, off, rank, list, r0, nr, T, N, k, k_pad));
+                  bwd_place<<<dim3(gp), 256, 0, stream>>>(idx, off, rank, list, cnt,
+                                                          use_list ? touched : nullptr, nkeys, r0, nr,
+                                                          T, N, k, k_pad));
+        // one wave per cache row, or per listed token (at most npairs of them)
+        const long long nred = use_list ? npairs : nkeys;
         DSA_TIMED("bwd_reduce", stream,
-                  bwd_reduce<<<dim3((unsigned)((nkeys + 3) / 4)), 256, 0, stream>>>(contrib, cnt, off,
-                                                                                    list, dkv, nkeys));
+                  bwd_reduce<<<dim3((unsigned)((nred + 3) / 4)), 256, 0, stream>>>(
+                      contrib, cnt, off, list, use_list ? touched : nullptr, dkv, nkeys));
         st = launch_status();
         if (st != DSA_OK) return st;
     }

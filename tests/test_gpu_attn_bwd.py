@@ -223,6 +223,18 @@ def test_bf16_decode_shaped_batch():
     _run_all_rows(wl, _random_idx(16, 1, 2500, 2048, rng), 8, "decode-shaped", False)
 
 
+def test_bf16_long_cache_few_rows():
+    # 4 rows over 2 x 30000 cache rows: far more rows than selected slots, so
+    # the per-token sum runs over the list of selected tokens; junk, a
+    # duplicated token and an empty row included
+    wl = WORKLOADS["prefill_8k"].with_(B=2, T=2, N=30000, k=512)
+    rng = np.random.default_rng(18)
+    idx = _random_idx(2, 2, 30000, 512, rng, junk=True)
+    idx[1, 0, 5:25] = idx[1, 0, 4]              # one token in 21 slots
+    idx[0, 1] = -1                              # a row with no valid slot
+    _run_all_rows(wl, idx, 9, "long cache, few rows", False)
+
+
 def _causal_random_idx(T, N, q_offset, k, rng):
     idx = np.full((1, T, k), -1, dtype=np.int32)
     for t in range(T):
