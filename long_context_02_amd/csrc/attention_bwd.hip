@@ -22,10 +22,11 @@
 //    as [row][tile][head][32 slots] for the second kernel, and dS feeds
 //    dq += dS C (36 MFMAs, the latent and rope columns read transposed from
 //    the gathered tile).  dq (fp32) stays in AGPRs until the end.
-//  * sparse_mla_bwd_dkv: one workgroup per query row.  Q and dO of the row
-//    are staged through LDS once and kept in VGPRs as transposed fragments
-//    (head-major K dimension); wave w owns output columns 128w..128w+127 of
-//    the latent part and the rope column block 16w..16w+15.  Per tile the
+//  * sparse_mla_bwd_dkv: one workgroup (8 waves, two per SIMD) per query
+//    row.  Q and dO of the row are staged through LDS once and kept in VGPRs
+//    as transposed fragments (head-major K dimension); wave w owns output
+//    columns 64w..64w+63 of the latent part and waves 0..3 the rope column
+//    blocks 16w..16w+15.  Per tile the
 //    P and dS blocks are staged in LDS and read transposed as the A operand
 //    (key x head); each slot's 576-wide vector dS^T q + P^T dO leaves the
 //    kernel as one contiguous bf16 row of the workspace.
@@ -59,6 +60,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // indices of one row into sidx (padded with -1 to a whole tile); returns the
 // position of the last valid slot (-1 if none)
+template <int NTH>
 __device__ __forceinline__ int load_slots(const int32_t* __restrict__ idx_row, int k, int N,
                                           int32_t* sidx, int* s_last) {
     const int tid = threadIdx.x;
@@ -67,16 +69,16 @@ __device__ __forceinline__ int load_slots(const int32_t* __restrict__ idx_row, i
     int my_last = -1;
     const int k_pad = (k + TK - 1) / TK * TK;
     // every load is issued before the first is waited for
-    constexpr int PER = (SLOTS + NT - 1) / NT;
+    constexpr int PER = (SLOTS + NTH - 1) / NTH;
     int id[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * NT;
+        const int i = tid + j * NTH;
         id[j] = i < k ? idx_row[i] : -1;
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * NT;
+        const int i = tid + j * NTH;
         if (i < k_pad) {
             sidx[i] = id[j];
             if (id[j] >= 0 && id[j] < N) my_last = i;
@@ -116,7 +118,7 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
     const uint16_t* __restrict__ kv_b = kv + (size_t)b * N * DQK;
     const int head = hg * HG + 16 * wave + m;  // this lane's head in S^T / dP^T
 
-    const int last = load_slots(idx + row * k, k, N, sidx, &s_last);
+    const int last = load_slots<NT>(idx + row * k, k, N, sidx, &s_last);
     const int n_tiles = (last + TK) / TK;
     const int dummy = last >= 0 ? sidx[last] : 0;
 
@@ -341,9 +343,10 @@ constexpr int SPITCH = 2 * DQK + 16;  // LDS pitch of a staged contribution row
 // LDS pitch of a staged P or dS tile row (32 slots = 64 bytes, padded so that
 // the four row groups of a transposed fragment read fall on different banks)
 constexpr int TPITCH = 96;
+constexpr int NTK = 512;  // threads of the dkv kernel (8 waves, 2 per SIMD)
 constexpr int TILE_LDS = H * TPITCH;  // 12 KiB
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NTK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_mla_bwd_dkv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
                         const int32_t* __restrict__ idx, const uint16_t* __restrict__ ws_p,
                         const uint16_t* __restrict__ ws_ds, uint16_t* __restrict__ contrib,
@@ -355,12 +358,10 @@ void sparse_mla_bwd_dkv(const uint16_t* __restrict__ q, const uint16_t* __restri
     const int lrow = blockIdx.x;
     if (lrow >= rows) return;
     const size_t row = (size_t)row0 + lrow;
-    const int b = (int)(row / (unsigned)T);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, g = lane >> 4;
-    (void)b;
 
-    const int last = load_slots(idx + row * k, k, N, sidx, &s_last);
+    const int last = load_slots<NTK>(idx + row * k, k, N, sidx, &s_last);
     const int n_tiles = (last + TK) / TK;
     if (n_tiles == 0) return;
 
@@ -377,62 +378,57 @@ void sparse_mla_bwd_dkv(const uint16_t* __restrict__ q, const uint16_t* __restri
         return as_bf16x8(vv);
     };
 
-    // this wave's column blocks: latent blocks 8w..8w+7 (value and key
-    // parts) and rope block 32 + w (key part only)
-    bf16x8 qt[9][4], ot[8][4];
+    // this wave's column blocks: latent blocks 4w..4w+3 (value and key
+    // parts) and, for waves 0..3, rope block 32 + w (key part only)
+    const bool rope = wave < 4;
+    auto qcb = [&](int j) __attribute__((always_inline)) { return j < 4 ? 4 * wave + j : 32 + (wave & 3); };
+    bf16x8 qt[5][4], ot[4][4];
     {
-        // (fixed trip counts, unrolled so that each thread's loads are in
-        // flight together)
         const uint16_t* qr = q + row * H * DQK;
-#pragma unroll 12
-        for (int it = 0; it < H * (DQK / 8) / NT; ++it) {
-            const int c = tid + it * NT;
+#pragma unroll 18
+        for (int it = 0; it < H * (DQK / 8) / NTK; ++it) {
+            const int c = tid + it * NTK;
             const int r = c / (DQK / 8), cc = c % (DQK / 8);
             *reinterpret_cast<uint4*>(buf + r * QPITCH + 16 * cc) =
                 *reinterpret_cast<const uint4*>(qr + r * DQK + 8 * cc);
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 9; ++j)
+        for (int j = 0; j < 5; ++j)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qt[j][kk] = tfrag(QPITCH, j < 8 ? 8 * wave + j : 32 + wave, kk);
+            for (int kk = 0; kk < 4; ++kk) qt[j][kk] = tfrag(QPITCH, qcb(j), kk);
         __syncthreads();
         const uint16_t* dr = dout + row * H * DV;
 #pragma unroll 16
-        for (int it = 0; it < H * (DV / 8) / NT; ++it) {
-            const int c = tid + it * NT;
+        for (int it = 0; it < H * (DV / 8) / NTK; ++it) {
+            const int c = tid + it * NTK;
             const int r = c / (DV / 8), cc = c % (DV / 8);
             *reinterpret_cast<uint4*>(buf + r * OPITCH + 16 * cc) =
                 *reinterpret_cast<const uint4*>(dr + r * DV + 8 * cc);
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) ot[j][kk] = tfrag(OPITCH, 8 * wave + j, kk);
+            for (int kk = 0; kk < 4; ++kk) ot[j][kk] = tfrag(OPITCH, 4 * wave + j, kk);
         __syncthreads();
     }
 
     // P and dS tiles ([128 heads][32 slots] bf16, 8 KiB each) staged in two
-    // buffers, each row padded to TPITCH bytes; each thread moves 2 x 16
-    // bytes of each
+    // buffers, each row padded to TPITCH bytes; each thread moves 16 bytes
+    // of each
     const size_t tile0 = (size_t)lrow * ntile;
-    uint4 rp0, rp1, rd0, rd1;
+    uint4 rp, rd;
     auto fetch = [&](int tile) __attribute__((always_inline)) {
-        const uint4* sp = reinterpret_cast<const uint4*>(ws_p + (tile0 + tile) * TILE_ELEMS);
-        const uint4* sd = reinterpret_cast<const uint4*>(ws_ds + (tile0 + tile) * TILE_ELEMS);
-        rp0 = sp[tid];
-        rp1 = sp[tid + NT];
-        rd0 = sd[tid];
-        rd1 = sd[tid + NT];
+        rp = reinterpret_cast<const uint4*>(ws_p + (tile0 + tile) * TILE_ELEMS)[tid];
+        rd = reinterpret_cast<const uint4*>(ws_ds + (tile0 + tile) * TILE_ELEMS)[tid];
     };
     auto put = [&](int slot) __attribute__((always_inline)) {
         uint8_t* bp = buf + slot * 2 * TILE_LDS + (tid >> 2) * TPITCH + 16 * (tid & 3);
-        *reinterpret_cast<uint4*>(bp) = rp0;
-        *reinterpret_cast<uint4*>(bp + 64 * TPITCH) = rp1;
-        *reinterpret_cast<uint4*>(bp + TILE_LDS) = rd0;
-        *reinterpret_cast<uint4*>(bp + TILE_LDS + 64 * TPITCH) = rd1;
+        *reinterpret_cast<uint4*>(bp) = rp;
+        *reinterpret_cast<uint4*>(bp + TILE_LDS) = rd;
     };
+    static_assert(NTK * 8 == TILE_ELEMS, "one 16-byte piece of each tile per thread");
     // A fragments (key x head): slots 16*kb + m, heads {4g..4g+3,
     // 16+4g..16+4g+3} + 32*kk, from a [head][32 slots] tile
     auto afrag = [&](const uint8_t* tb, int kb, int kk) __attribute__((always_inline)) -> bf16x8 {
@@ -462,22 +458,24 @@ void sparse_mla_bwd_dkv(const uint16_t* __restrict__ q, const uint16_t* __restri
                 ad[kk] = afrag(tp + TILE_LDS, kb, kk);
                 ap[kk] = afrag(tp, kb, kk);
             }
-            f32x4 acc[9];
+            f32x4 acc[5];
 #pragma unroll
-            for (int j = 0; j < 9; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 5; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-                for (int j = 0; j < 9; ++j) acc[j] = mfma_bf16(ad[kk], qt[j][kk], acc[j]);
+                for (int j = 0; j < 4; ++j) acc[j] = mfma_bf16(ad[kk], qt[j][kk], acc[j]);
+                if (rope) acc[4] = mfma_bf16(ad[kk], qt[4][kk], acc[4]);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = mfma_bf16(ap[kk], ot[j][kk], acc[j]);
+                for (int j = 0; j < 4; ++j) acc[j] = mfma_bf16(ap[kk], ot[j][kk], acc[j]);
             }
             // rows of acc: slots 16*kb + 4g + i, column 16*cb + m.  Lanes m and
             // m^1 trade one value so that each writes two adjacent columns of
             // one slot row (a 32-bit LDS store) into the staged tile.
 #pragma unroll
-            for (int j = 0; j < 9; ++j) {
-                const int col = 16 * (j < 8 ? 8 * wave + j : 32 + wave) + (m & ~1);
+            for (int j = 0; j < 5; ++j) {
+                if (j == 4 && !rope) break;
+                const int col = 16 * qcb(j) + (m & ~1);
 #pragma unroll
                 for (int ip = 0; ip < 2; ++ip) {
                     const float a0 = acc[j][2 * ip], a1 = acc[j][2 * ip + 1];
@@ -494,11 +492,13 @@ void sparse_mla_bwd_dkv(const uint16_t* __restrict__ q, const uint16_t* __restri
         __syncthreads();
         uint16_t* dst = contrib + ((size_t)lrow * (ntile * TK) + t * TK) * DQK;
 #pragma unroll
-        for (int it = 0; it < TK * (DQK / 8) / NT; ++it) {
-            const int c = tid + it * NT;
-            const int r = c / (DQK / 8), cc = c % (DQK / 8);
-            *reinterpret_cast<uint4*>(dst + r * DQK + 8 * cc) =
-                *reinterpret_cast<const uint4*>(stg + r * SPITCH + 16 * cc);
+        for (int it = 0; it < (TK * (DQK / 8) + NTK - 1) / NTK; ++it) {
+            const int c = tid + it * NTK;
+            if (c < TK * (DQK / 8)) {
+                const int r = c / (DQK / 8), cc = c % (DQK / 8);
+                *reinterpret_cast<uint4*>(dst + r * DQK + 8 * cc) =
+                    *reinterpret_cast<const uint4*>(stg + r * SPITCH + 16 * cc);
+            }
         }
         if (t + 1 < n_tiles) put((t + 1) & 1);
         __syncthreads();
@@ -771,7 +771,7 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
                       qq, kk, idx, oo, lse, dd, dq, ws_p, ws_ds, r0, nr, T, N, k, ntile,
                       sm_scale * kLog2e, sm_scale));
         DSA_TIMED("sparse_mla_bwd_dkv", stream,
-                  sparse_mla_bwd_dkv<<<dim3((unsigned)nr), NT, 0, stream>>>(
+                  sparse_mla_bwd_dkv<<<dim3((unsigned)nr), NTK, 0, stream>>>(
                       qq, dd, idx, ws_p, ws_ds, contrib, r0, nr, T, N, k, ntile));
         DSA_TIMED("bwd_count", stream,
                   bwd_count<<<dim3(gp), 256, 0, stream>>>(idx, cnt, rank, r0, nr, T, N, k, k_pad));
