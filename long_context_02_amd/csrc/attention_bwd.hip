@@ -31,9 +31,10 @@
 //    (key x head); each slot's 576-wide vector dS^T q + P^T dO leaves the
 //    kernel as one contiguous bf16 row of the workspace.
 //  * the vectors are summed per token without atomics on dkv: a counting
-//    sort lists the (row, slot) pairs of every token (bwd_count with ranks,
-//    a three-kernel exclusive scan, bwd_place), then bwd_reduce gives each
-//    token one wave that adds its rows in fp32 and adds the sum to dkv.
+//    sort lists the (row, slot) pairs of every token (the counts and each
+//    slot's rank from sparse_mla_bwd_dq, a three-kernel exclusive scan,
+//    bwd_place), then bwd_reduce gives each token one wave that adds its
+//    rows in fp32 and adds the sum to dkv.
 //    (fp32 atomic adds straight from sparse_mla_bwd_dkv, one per element of
 //    every slot vector, took about 3.7 times as long as plain stores of the
 //    same values at the chunked-prefill shape.)
@@ -94,8 +95,9 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
                        const int32_t* __restrict__ idx, const uint16_t* __restrict__ out,
                        const float* __restrict__ lse, const uint16_t* __restrict__ dout,
                        float* __restrict__ dq, uint16_t* __restrict__ ws_p,
-                       uint16_t* __restrict__ ws_ds, long long row0, int rows, int T, int N, int k,
-                       int ntile, float scale_log2, float sm_scale) {
+                       uint16_t* __restrict__ ws_ds, int* __restrict__ cnt, int* __restrict__ rank,
+                       long long row0, int rows, int T, int N, int k, int ntile, float scale_log2,
+                       float sm_scale) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
@@ -121,6 +123,26 @@ void sparse_mla_bwd_dq(const uint16_t* __restrict__ q, const uint16_t* __restric
     const int last = load_slots<NT>(idx + row * k, k, N, sidx, &s_last);
     const int n_tiles = (last + TK) / TK;
     const int dummy = last >= 0 ? sidx[last] : 0;
+
+    // the per-token count of the dkv sum: the first head half's workgroup
+    // counts the row's valid slots into cnt and keeps each slot's rank (the
+    // atomics' latency overlaps the gather and products that follow)
+    if (hg == 0) {
+        const int k_pad = ntile * TK;
+        constexpr int PER = (SLOTS + NT - 1) / NT;
+        int rr[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * NT;
+            const int sid = i < k_pad ? sidx[i] : -1;
+            rr[j] = (unsigned)sid < (unsigned)N ? atomicAdd(&cnt[(long long)b * N + sid], 1) : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * NT;
+            if (i < k_pad) rank[(size_t)lrow * k_pad + i] = rr[j];
+        }
+    }
 
     // LDS offsets inside a stage (same tile layout as the forward):
     // key fragments (chunk 4*ks + g of row m), rope fragments, and the
@@ -519,27 +541,13 @@ __global__ __launch_bounds__(256) void zero_i32(int* __restrict__ p, size_t n) {
 // ---------------------------------------------------------------------------
 // Sum of the contribution rows per token.  A pair p = lrow * k_pad + slot of
 // the block's rows selects token key = b * N + idx; the pairs of each token
-// are listed contiguously (counting sort: count with ranks, exclusive scan of
-// the counts, placement), then one wave per token adds its rows.  When the
+// are listed contiguously (counting sort: the counts with ranks, taken by
+// sparse_mla_bwd_dq, an exclusive scan of the counts, placement), then one
+// wave per token adds its rows.  When the
 // batch has many more cache rows than a block has pairs (decode-shaped
 // batches), placement also lists the tokens that have pairs (the pair of rank
 // 0 appends its token; cnt[nkeys] counts them), so the sum runs over the
 // selected tokens only, not over every row of the cache.
-
-__global__ __launch_bounds__(256) void bwd_count(const int32_t* __restrict__ idx, int* __restrict__ cnt,
-                                                int* __restrict__ rank, long long row0, int rows, int T,
-                                                int N, int k, int k_pad) {
-    const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (p >= (long long)rows * k_pad) return;
-    const int lrow = (int)(p / k_pad), slot = (int)(p % k_pad);
-    int r = -1;
-    if (slot < k) {
-        const long long row = row0 + lrow;
-        const int id = idx[row * k + slot];
-        if ((unsigned)id < (unsigned)N) r = atomicAdd(&cnt[(row / T) * N + id], 1);
-    }
-    rank[p] = r;
-}
 
 constexpr int SCAN_CHUNK = 2048;  // counts per scan workgroup (256 threads x 8)
 
@@ -768,13 +776,11 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
                              stream>>>(cnt, (size_t)nkeys + 1));
         DSA_TIMED("sparse_mla_bwd_dq", stream,
                   sparse_mla_bwd_dq<<<dim3((unsigned)((nr + 7) / 8 * 16)), NT, 0, stream>>>(
-                      qq, kk, idx, oo, lse, dd, dq, ws_p, ws_ds, r0, nr, T, N, k, ntile,
+                      qq, kk, idx, oo, lse, dd, dq, ws_p, ws_ds, cnt, rank, r0, nr, T, N, k, ntile,
                       sm_scale * kLog2e, sm_scale));
         DSA_TIMED("sparse_mla_bwd_dkv", stream,
                   sparse_mla_bwd_dkv<<<dim3((unsigned)nr), NTK, 0, stream>>>(
                       qq, dd, idx, ws_p, ws_ds, contrib, r0, nr, T, N, k, ntile));
-        DSA_TIMED("bwd_count", stream,
-                  bwd_count<<<dim3(gp), 256, 0, stream>>>(idx, cnt, rank, r0, nr, T, N, k, k_pad));
         DSA_TIMED("scan_chunk_sums", stream,
                   scan_chunk_sums<<<dim3(nchunks), 256, 0, stream>>>(cnt, sums, nkeys));
         DSA_TIMED("scan_sums", stream, scan_sums<<<dim3(1), 256, 0, stream>>>(sums, (int)nchunks));
