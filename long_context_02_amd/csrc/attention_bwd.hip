@@ -658,13 +658,21 @@ __device__ __forceinline__ void add_bf16x8(float* a, const uint4& x) {
 __global__ __launch_bounds__(256) void bwd_reduce(const uint16_t* __restrict__ contrib,
                                                  const int* __restrict__ cnt, const int* __restrict__ off,
                                                  const int* __restrict__ list, const int* __restrict__ touched,
-                                                 float* __restrict__ dkv, long long nkeys) {
+                                                 float* __restrict__ dkv, long long nkeys, int overwrite) {
     const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= (touched ? (long long)cnt[nkeys] : nkeys)) return;
     const long long key = touched ? (long long)touched[w] : w;
     const int n = cnt[key];
-    if (n == 0) return;
     const int lane = threadIdx.x & 63;
+    if (n == 0) {
+        // (overwrite: the first block of a call that visits every cache row
+        // writes the whole of dkv, zeros for the rows without pairs)
+        if (overwrite) {
+            float4* d = reinterpret_cast<float4*>(dkv + key * DQK);
+            for (int c = lane; c < DQK / 4; c += 64) d[c] = float4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
     const bool two = lane < DQK / 8 - 64;
     const int o = off[key];
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -690,11 +698,12 @@ __global__ __launch_bounds__(256) void bwd_reduce(const uint16_t* __restrict__ c
         }
     }
     float4* d = reinterpret_cast<float4*>(dkv + key * DQK);
-    float4 d0 = d[2 * lane], d1 = d[2 * lane + 1];
+    const float4 zero = {0.f, 0.f, 0.f, 0.f};
+    float4 d0 = overwrite ? zero : d[2 * lane], d1 = overwrite ? zero : d[2 * lane + 1];
     d[2 * lane] = float4{d0.x + a[0], d0.y + a[1], d0.z + a[2], d0.w + a[3]};
     d[2 * lane + 1] = float4{d1.x + a[4], d1.y + a[5], d1.z + a[6], d1.w + a[7]};
     if (two) {
-        float4 e0v = d[2 * (lane + 64)], e1v = d[2 * (lane + 64) + 1];
+        float4 e0v = overwrite ? zero : d[2 * (lane + 64)], e1v = overwrite ? zero : d[2 * (lane + 64) + 1];
         d[2 * (lane + 64)] = float4{e0v.x + b[0], e0v.y + b[1], e0v.z + b[2], e0v.w + b[3]};
         d[2 * (lane + 64) + 1] = float4{e1v.x + b[4], e1v.y + b[5], e1v.z + b[6], e1v.w + b[7]};
     }
@@ -760,17 +769,24 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
     const auto* dd = static_cast<const uint16_t*>(dout);
     const unsigned nchunks = (unsigned)((nkeys + SCAN_CHUNK - 1) / SCAN_CHUNK);
 
-    const size_t n4 = (size_t)nkeys * DQK / 4;
-    DSA_TIMED("zero_f32", stream,
-              zero_f32<<<dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 8192)), 256, 0, stream>>>(
-                  reinterpret_cast<float4*>(dkv), n4));
-    dsa_status st = launch_status();
-    if (st != DSA_OK) return st;
+    // dkv starts at zero: cleared here when the first block sums over a
+    // list of tokens, otherwise written whole by the first block's sum
+    const bool first_list = nkeys > 4 * (long long)rb * k_pad;
+    dsa_status st = DSA_OK;
+    if (first_list) {
+        const size_t n4 = (size_t)nkeys * DQK / 4;
+        DSA_TIMED("zero_f32", stream,
+                  zero_f32<<<dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 8192)), 256, 0, stream>>>(
+                      reinterpret_cast<float4*>(dkv), n4));
+        st = launch_status();
+        if (st != DSA_OK) return st;
+    }
     for (long long r0 = 0; r0 < rows; r0 += rb) {
         const int nr = (int)std::min<long long>(rb, rows - r0);
         const long long npairs = (long long)nr * k_pad;
         const unsigned gp = (unsigned)((npairs + 255) / 256);
         const bool use_list = nkeys > 4 * npairs;  // most cache rows unselected
+        const int overwrite = r0 == 0 && !use_list ? 1 : 0;
         DSA_TIMED("zero_i32", stream,
                   zero_i32<<<dim3((unsigned)std::min<long long>((nkeys + 256) / 256, 8192)), 256, 0,
                              stream>>>(cnt, (size_t)nkeys + 1));
@@ -794,7 +810,7 @@ dsa_status launch_attn_bwd_bf16(const void* q, const void* kv, const int32_t* id
         const long long nred = use_list ? npairs : nkeys;
         DSA_TIMED("bwd_reduce", stream,
                   bwd_reduce<<<dim3((unsigned)((nred + 3) / 4)), 256, 0, stream>>>(
-                      contrib, cnt, off, list, use_list ? touched : nullptr, dkv, nkeys));
+                      contrib, cnt, off, list, use_list ? touched : nullptr, dkv, nkeys, overwrite));
         st = launch_status();
         if (st != DSA_OK) return st;
     }

@@ -135,7 +135,10 @@ def _run_all_rows(wl, idx_np, seed, where, use_gpu_forward):
         out = torch.from_numpy(o_ref).to(torch.bfloat16).to(dev)
         lse = torch.from_numpy(l_ref).to(torch.float32).to(dev)
     print(f"[attn_bwd] {where}", flush=True)
-    dq, dkv = dsa.sparse_mla_attn_bwd(q, kv, idx, out, lse, dout, wl.sm_scale)
+    # NaN-poisoned outputs: every element must be written
+    dq = torch.full((wl.B, wl.T, wl.H, wl.d_qk), float("nan"), dtype=torch.float32, device=dev)
+    dkv = torch.full((wl.B, wl.N, wl.d_qk), float("nan"), dtype=torch.float32, device=dev)
+    dsa.sparse_mla_attn_bwd(q, kv, idx, out, lse, dout, wl.sm_scale, dq=dq, dkv=dkv)
     torch.cuda.synchronize()
     dq_g, dkv_g = np64(dq), np64(dkv)
     assert np.isfinite(dq_g).all() and np.isfinite(dkv_g).all(), where
