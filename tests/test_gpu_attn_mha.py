@@ -133,21 +133,30 @@ def test_ragged_up_projection_rows_and_two_sequences():
     check_lse(np64(lse).reshape(6, 128), ref_l, True, "mha ragged")
 
 
-def test_prefill_8k_selection_sampled_rows():
-    # the benchmark's configuration: prefill at L = 8192 on the path's own
-    # selection, checked on sampled rows
+@pytest.mark.parametrize("name", ["prefill_8k", "chunk_128k"])
+def test_full_size_selection_sampled_rows(name):
+    # the benchmark's configurations (prefill at L = 8192; 4096 new tokens on
+    # a 131072-row cache) on the path's own selection, checked on sampled
+    # rows: at prefill the first and last rows, the rows around t = k and
+    # random ones; on the chunk the first and last rows and two random ones
     dev = gpu_device()
-    wl = WORKLOADS["prefill_8k"]
-    print("[mha] prefill_8k sampled rows", flush=True)
+    wl = WORKLOADS[name]
+    print(f"[mha] {name} sampled rows", flush=True)
     g = _inputs(wl, 23, dev)
     idx_t = dsa.indexer_select(g["q_idx"], g["k_idx"], g["w"], wl.k, wl.q_offset,
                                q_idx_scale=g["q_idx_scale"], k_idx_scale=g["k_idx_scale"])
     out, lse = _run(g, idx_t)
     torch.cuda.synchronize()
     rng = np.random.default_rng(23)
-    rows = [(0, t) for t in sample_rows(wl.T, wl.k, rng, extra=4)]
+    if wl.q_offset == 0:
+        ts = sample_rows(wl.T, wl.k, rng, extra=4)
+    else:
+        ts = sorted({0, wl.T - 1, *[int(t) for t in rng.integers(1, wl.T - 1, 2)]})
+    rows = [(0, t) for t in ts]
     idx = idx_t.cpu().numpy()
     ref_o, ref_l = _oracle_rows(g, idx, rows)
     ts = [t for _, t in rows]
-    check_attention(np64(out[0, ts]), ref_o, True, "mha prefill_8k")
-    check_lse(np64(lse[0, ts]), ref_l, True, "mha prefill_8k")
+    check_attention(np64(out[0, ts]), ref_o, True, f"mha {name}")
+    check_lse(np64(lse[0, ts]), ref_l, True, f"mha {name}")
+    del g, out, lse, idx_t
+    torch.cuda.empty_cache()
