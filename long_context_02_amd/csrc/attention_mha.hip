@@ -60,9 +60,9 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // consecutive rows hit distinct banks.
 // bf16 v_mfma_f32_32x32x16: A = 16 bytes of a latent row, B = 16 bytes of a
 // weight row (both k-contiguous).  Results go out in bf16 straight from the
-// accumulators, adjacent lanes pairing columns by DPP (4-byte streaming
-// stores: the 8 GiB of per-head rows would only evict the latent rows and
-// weights from the caches).
+// accumulators through LDS (adjacent lanes pairing columns by DPP) and out as
+// 16-byte streaming stores (the 8 GiB of per-head rows would only evict the
+// latent rows and weights from the caches).
 // Workgroup order: workgroups are handed to the 8 XCDs in turn, so XCD x
 // takes row blocks x, x + 8, ...; along one XCD the head runs fastest within
 // a group of UP_HG heads, so the workgroups resident on an XCD at once share
@@ -74,6 +74,8 @@ constexpr int UP_COLS = 2 * DN;       // output columns per workgroup (one head:
 constexpr int UP_BK = 32;             // k per chunk
 constexpr int UP_A = UP_ROWS * UP_BK; // bf16 per A chunk
 constexpr int UP_B = UP_COLS * UP_BK; // bf16 per B chunk
+constexpr int UP_OPITCH = 2 * 128 + 16; // LDS bytes per staged output row (128 bf16 + pad)
+static_assert(4 * 32 * UP_OPITCH <= 2 * (2 * UP_A + 2 * UP_B), "output staging fits the chunk buffers");
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -86,8 +88,11 @@ __global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restr
                                                       const uint16_t* __restrict__ w_uv,
                                                       uint16_t* __restrict__ kh,
                                                       uint16_t* __restrict__ vh, long long rows) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][UP_A];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][UP_B];
+    // the chunk buffers (A: 2 x UP_A, then B: 2 x UP_B); after the
+    // contraction the same bytes stage the output rows
+    __shared__ __attribute__((aligned(16))) uint16_t lds_ab[2 * UP_A + 2 * UP_B];
+    uint16_t* const lds_a[2] = {lds_ab, lds_ab + UP_A};
+    uint16_t* const lds_b[2] = {lds_ab + 2 * UP_A, lds_ab + 2 * UP_A + UP_B};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int s_x = blockIdx.x >> 3;  // position along XCD blockIdx.x % 8
     const int h = blockIdx.y * UP_HG + s_x % UP_HG;
@@ -195,10 +200,16 @@ __global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restr
     // + 4 half + e % 4, column 32 cb + i32 of the wave's 128.  Adjacent lanes
     // (i32 even / odd) trade one value so that the even lane holds columns
     // i32, i32 + 1 of row e and the odd lane columns i32 - 1, i32 of row e + 1.
+    // Each half of the wave's rows (32 rows x 128 columns, bf16) is staged in
+    // the wave's own LDS region and leaves as 16-byte pieces: lane l takes
+    // piece l % 16 of row 4 j + l / 16, so 16 lanes write one 256-byte row
+    // segment.
     const bool odd = (i32 & 1) != 0;
     uint16_t* const base = wc == 0 ? kh : vh;
+    uint8_t* const stg = reinterpret_cast<uint8_t*>(lds_ab) + wave * (32 * UP_OPITCH);
 #pragma unroll
-    for (int rb2 = 0; rb2 < 2; ++rb2)
+    for (int rb2 = 0; rb2 < 2; ++rb2) {
+        __syncthreads();  // (the chunk buffers, then the previous half, are read)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -208,14 +219,21 @@ __global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restr
                 const float recv = __builtin_bit_cast(
                     float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xf, 0xf, false));
                 const float lo = odd ? recv : x0, hi = odd ? x1 : recv;
-                const int r = 64 * wr + 32 * rb2 + 8 * (e >> 2) + 4 * half + (e & 3) + (odd ? 1 : 0);
-                const long long gr = r0 + r;
-                if (gr < rows) {
-                    const uint32_t pk = (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
-                    __builtin_nontemporal_store(
-                        pk, reinterpret_cast<uint32_t*>(base + ((size_t)gr * H + h) * DN + 32 * cb + (i32 & ~1)));
-                }
+                const int rl = 8 * (e >> 2) + 4 * half + (e & 3) + (odd ? 1 : 0);
+                const uint32_t pk = (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+                *reinterpret_cast<uint32_t*>(stg + rl * UP_OPITCH + 2 * (32 * cb + (i32 & ~1))) = pk;
             }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int rl = 4 * j + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * UP_OPITCH + 16 * (lane & 15));
+            const long long gr = r0 + 64 * wr + 32 * rb2 + rl;
+            if (gr < rows)
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4*>(base + ((size_t)gr * H + h) * DN + 8 * (lane & 15)));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
