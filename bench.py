@@ -72,7 +72,7 @@ KERNEL_SOURCES = {
     "topk_seg": ("topk.hip", "indexer_math.h", "topk_select.h"),
     "sparse_mla_attn_bf16": _ATT, "attn_combine": _ATT,
     "attn_bwd": ("attention_bwd.hip", "attn_common.h"),
-    "mha": ("attention_mha.hip",),
+    "mha": ("attention_mha.hip",), "sparse_mha_attn": ("attention_mha.hip",),
 }
 
 
@@ -580,12 +580,14 @@ def time_attn_mha(wl, g, idx, steps, stream, seed=0):
             ach = up_flop / (t / 1e3) / 1e12
             res["kernels"][name] = {"ms": round(t, 4), "bound": "mfma", "achieved": round(ach, 1),
                                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                                    "algorithmic_flop": up_flop, "algorithmic_bytes": up_bytes}
+                                    "algorithmic_flop": up_flop, "algorithmic_bytes": up_bytes,
+                                    "traffic": measured_traffic(name, wl)}
         else:
             ach = gather_bytes / (t / 1e3) / 1e9
             res["kernels"][name] = {"ms": round(t, 4), "bound": "hbm", "achieved": round(ach, 1),
                                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                                     "algorithmic_bytes": gather_bytes,
+                                    "traffic": measured_traffic(name, wl),
                                     "note": "per-head rows gathered once per (query, token, head); "
                                             "rows shared by nearby queries may come from the caches"}
     return {"attn_mha": res}
