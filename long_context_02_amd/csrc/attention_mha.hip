@@ -44,14 +44,14 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 
 // ---------------------------------------------------------------------------
 // Up-projection: out[row, col] = c[row, :512] . W[col, :] for the 256 output
-// columns of one head (W_UK[h]'s 128 rows, then W_UV[h]'s) and 128 latent rows
-// per workgroup (4 waves: wave w takes rows 64 (w / 2) .. +63 and the key
+// columns of one head (W_UK[h]'s 128 rows, then W_UV[h]'s) and 256 latent rows
+// per workgroup (8 waves: wave w takes rows 64 (w / 2) .. +63 and the key
 // (w even) or value (w odd) columns; 2 x 4 blocks of 32 x 32 fp32 per wave).
-// The contraction runs in 16 chunks of 32 k: each chunk's 128 latent rows
+// The contraction runs in 16 chunks of 32 k: each chunk's 256 latent rows
 // and 256 weight rows (64 bytes each) are staged in LDS, double-buffered,
 // and its global loads are issued two chunks ahead of its product (two
-// register sets), so two chunks' MFMA work covers their latency; two
-// workgroups share a CU (48 KiB of LDS each).  A row's four 16-byte pieces
+// register sets), so two chunks' MFMA work covers their latency; one
+// workgroup (two waves per SIMD) per CU.  A row's four 16-byte pieces
 // sit at slot q ^ ((r / 4) % 4), so the 16 lanes that read one piece of 16
 // consecutive rows hit distinct banks.
 // bf16 v_mfma_f32_32x32x16: A = 16 bytes of a latent row, B = 16 bytes of a
@@ -63,7 +63,8 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // takes row blocks x, x + 8, ...; along one XCD the head runs fastest within
 // a group of UP_HG heads, so the workgroups resident on an XCD at once share
 // latent row blocks through its L2 while the group's weights stay there too.
-constexpr int UP_ROWS = 128;          // latent rows per workgroup
+constexpr int UP_ROWS = 256;          // latent rows per workgroup
+constexpr int UP_NT = 512;            // threads per workgroup (8 waves)
 constexpr int UP_HG = 8;              // heads per group (grid y = H / UP_HG)
 static_assert(H % UP_HG == 0, "head groups must tile the heads");
 constexpr int UP_COLS = 2 * DN;       // output columns per workgroup (one head: key + value)
@@ -71,7 +72,8 @@ constexpr int UP_BK = 32;             // k per chunk
 constexpr int UP_A = UP_ROWS * UP_BK; // bf16 per A chunk
 constexpr int UP_B = UP_COLS * UP_BK; // bf16 per B chunk
 constexpr int UP_OPITCH = 2 * 128 + 16; // LDS bytes per staged output row (128 bf16 + pad)
-static_assert(4 * 32 * UP_OPITCH <= 2 * (2 * UP_A + 2 * UP_B), "output staging fits the chunk buffers");
+constexpr int UP_LDS = 2 * (2 * UP_A + 2 * UP_B) > (UP_NT / 64) * 32 * UP_OPITCH
+                           ? 2 * (2 * UP_A + 2 * UP_B) : (UP_NT / 64) * 32 * UP_OPITCH;  // bytes
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -79,14 +81,14 @@ constexpr int kRawBuf = 0x00020000;  // buffer resource word 3: raw (untyped) 32
 
 __device__ __forceinline__ int up_slot(int r, int q) { return 4 * r + (q ^ ((r >> 2) & 3)); }
 
-__global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restrict__ kv,
+__global__ __launch_bounds__(UP_NT) void mha_up_project(const uint16_t* __restrict__ kv,
                                                       const uint16_t* __restrict__ w_uk,
                                                       const uint16_t* __restrict__ w_uv,
                                                       uint16_t* __restrict__ kh,
                                                       uint16_t* __restrict__ vh, long long rows) {
     // the chunk buffers (A: 2 x UP_A, then B: 2 x UP_B); after the
     // contraction the same bytes stage the output rows
-    __shared__ __attribute__((aligned(16))) uint16_t lds_ab[2 * UP_A + 2 * UP_B];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_ab[UP_LDS / 2];
     uint16_t* const lds_a[2] = {lds_ab, lds_ab + UP_A};
     uint16_t* const lds_b[2] = {lds_ab + 2 * UP_A, lds_ab + 2 * UP_A + UP_B};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -94,13 +96,14 @@ __global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restr
     const int h = blockIdx.y * UP_HG + s_x % UP_HG;
     const long long r0 = ((long long)(s_x / UP_HG) * 8 + (blockIdx.x & 7)) * UP_ROWS;
     if (r0 >= rows) return;
-    const int wr = wave >> 1, wc = wave & 1;  // row half, key / value columns
+    const int wr = wave >> 1, wc = wave & 1;  // row quarter, key / value columns
     const int i32 = lane & 31, half = lane >> 5;
 
-    // chunk loads through buffer resources: A = 128 latent rows x 4 pieces
-    // (2 per thread), B = 256 weight rows x 4 pieces (4 per thread); thread
-    // tid moves piece tid % 4 of rows tid / 4 + 64 j.  Latent rows past the
-    // end read as zeros (every offset sits in the range-checked vector offset).
+    // chunk loads through buffer resources: A = 256 latent rows x 4 pieces
+    // (2 per thread), B = 256 weight rows x 4 pieces (2 per thread: W_UK[h]'s
+    // row, then W_UV[h]'s); thread tid moves piece tid % 4 of rows tid / 4 +
+    // 128 j.  Latent rows past the end read as zeros (every offset sits in the
+    // range-checked vector offset).
     const int nrow = (int)(rows - r0 < UP_ROWS ? rows - r0 : UP_ROWS);
     const auto a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kv + (size_t)r0 * LAT_ROW), 0,
                                                         nrow * LAT_ROW * 2, kRawBuf);
@@ -111,22 +114,20 @@ __global__ __launch_bounds__(256, 2) void mha_up_project(const uint16_t* __restr
     const int pr = tid >> 2, pq = tid & 3;
     const int a_voff = pr * LAT_ROW * 2 + 16 * pq;
     const int b_voff = pr * DC * 2 + 16 * pq;
-    const int st_el = 8 * up_slot(pr, pq);  // + 64 rows = + 4096 bytes (the slot swizzle repeats)
-    struct Chunk { u32x4 a[2], b[4]; };
+    const int st_el = 8 * up_slot(pr, pq);  // + 128 rows = + 8192 bytes (the slot swizzle repeats)
+    struct Chunk { u32x4 a[2], b[2]; };
     auto load = [&](Chunk& c, int kc) __attribute__((always_inline)) {
         const int ko = UP_BK * 2 * kc;
         c.a[0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff + ko, 0, 0);
-        c.a[1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff + 64 * LAT_ROW * 2 + ko, 0, 0);
+        c.a[1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, a_voff + 128 * LAT_ROW * 2 + ko, 0, 0);
         c.b[0] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, b_voff + ko, 0, 0);
-        c.b[1] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, b_voff + 64 * DC * 2 + ko, 0, 0);
-        c.b[2] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, b_voff + ko, 0, 0);
-        c.b[3] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, b_voff + 64 * DC * 2 + ko, 0, 0);
+        c.b[1] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, b_voff + ko, 0, 0);
     };
     auto stage = [&](const Chunk& c, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&lds_a[buf][st_el + 2048 * j]) = c.a[j];
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&lds_a[buf][st_el + 4096 * j]) = c.a[j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&lds_b[buf][st_el + 2048 * j]) = c.b[j];
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&lds_b[buf][st_el + 4096 * j]) = c.b[j];
     };
 
     f32x16_t acc[2][4];
@@ -382,14 +383,14 @@ dsa_status launch_attn_mha_bf16(const void* q, const void* kv, const void* w_uk,
     const long long rows_kv = (long long)B * N;
     const long long rows_q = (long long)B * T;
     // up-projection grid: x = 8 XCDs x (row blocks per XCD) x UP_HG heads,
-    // 256 threads each; the x extent in threads must stay below 2^32
+    // UP_NT threads each; the x extent in threads must stay below 2^32
     const long long up_jb = ((rows_kv + UP_ROWS - 1) / UP_ROWS + 7) / 8;
-    if (rows_q > 0x7fffffffLL || up_jb * 8 * UP_HG * 256 > 0xffffffffLL) return DSA_ERR_UNSUPPORTED;
+    if (rows_q > 0x7fffffffLL || up_jb * 8 * UP_HG * UP_NT > 0xffffffffLL) return DSA_ERR_UNSUPPORTED;
     auto* kh = static_cast<uint16_t*>(workspace);
     auto* vh = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
                                            align_up((size_t)rows_kv * H * DN * sizeof(uint16_t)));
     DSA_TIMED("mha_up_project", stream,
-              mha_up_project<<<dim3((unsigned)(up_jb * 8 * UP_HG), H / UP_HG), 256, 0,
+              mha_up_project<<<dim3((unsigned)(up_jb * 8 * UP_HG), H / UP_HG), UP_NT, 0,
                                stream>>>(static_cast<const uint16_t*>(kv),
                                          static_cast<const uint16_t*>(w_uk),
                                          static_cast<const uint16_t*>(w_uv), kh, vh, rows_kv));

@@ -77,14 +77,16 @@ def test_small_batch_every_row():
     assert np.all(got_o[2] == 0) and np.all(np.isneginf(got_l[2]))
 
 
-@pytest.mark.parametrize("B,N", [(1, 130), (3, 77), (1, 128)])
+@pytest.mark.parametrize("B,N", [(1, 130), (3, 77), (1, 300), (2, 256)])
 def test_up_projected_rows_in_workspace(B, N):
     """The head-dependent key and value parts of every latent row, read back
     from the workspace (layout as the header states), against the oracle's
     float64 W_UK[h] c_s and W_UV[h] c_s: the kernel rounds fp32 sums to bf16,
     so each element is within 2^-8 of its size plus the fp32 summation error
-    of 512 terms.  B*N = 130 leaves a 2-row tail after one 128-row block,
-    231 a 103-row tail; 128 is one whole block."""
+    of 512 terms.  The up-projection takes latent rows 256 at a time, each
+    block's loads in two halves of 128 rows: B*N = 130 ends 2 rows into the
+    second half of its only block, 231 at 103 rows into it, 300 leaves a
+    44-row second block, 512 is two whole blocks."""
     dev = gpu_device()
     wl = WORKLOADS["prefill_8k"].with_(B=B, T=1, N=N, k=16)
     print(f"[mha] workspace rows B={B} N={N}", flush=True)
