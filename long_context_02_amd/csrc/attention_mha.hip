@@ -15,7 +15,7 @@
 //    (W_UK[h] c_s[:512], W_UV[h] c_s[:512]) of every latent row into the
 //    workspace (bf16, fp32 accumulation), a dense contraction on bf16 MFMA:
 //    out[token, col] = c[token, :512] . W[col, :] for the 256 output
-//    columns (128 key + 128 value) of one head and 128 tokens per workgroup.
+//    columns (128 key + 128 value) of one head and 256 tokens per workgroup.
 //    The rope part of the key is one part shared by every head: it is read
 //    from the latent row itself.
 //  * sparse_mha_attn: one workgroup per query token, 16 waves x 8 heads, 8
