@@ -388,15 +388,19 @@ __global__ __launch_bounds__(NT) void indexer_fp8_stream(
 
 // ---------------------------------------------------------------------------
 // Per-row threshold for the decode selection.  One 1024-thread workgroup per
-// row with more than k candidates scores S = min(1024, n_cand) keys spread
-// evenly over the row (key floor(i * n_cand / S)), with the stream layout's
-// arithmetic, and takes the key of its r-th largest sample score rounded
+// row with more than k candidates scores S = min(1024, n_cand) keys: all of
+// them for rows of fewer than 1024, otherwise 64 blocks of 16 consecutive
+// keys spread evenly over the row (block j starts at key
+// floor(j (n_cand - 16) / 63); a block's 2 KiB of keys come in one piece,
+// where 1024 single keys cost a memory round trip each), with the stream
+// layout's arithmetic, and takes the key of its r-th largest sample score rounded
 // down to 22 bits, r = mu + 6 sqrt(mu) + 8 with mu = S k / n_cand the
 // expected number of samples among the row's top k.  Keys at or above it
 // hold the row's top k unless the sample is far from typical, and the
 // selection checks that (count >= k) before trusting it.  Also clears the
 // row's candidate counter and overflow flag.
 constexpr int SMP = 1024;
+static_assert(SMP % 16 == 0, "the sample is whole 16-key blocks");
 constexpr int SMT = TT;  // threads (the block helpers of topk_select.h assume TT)
 
 __global__ __launch_bounds__(SMT) void indexer_sample_threshold(
@@ -432,7 +436,8 @@ __global__ __launch_bounds__(SMT) void indexer_sample_threshold(
 #pragma unroll
     for (int f = 0; f < FPW; ++f) {
         const int i = 16 * (FPW * wave + f) + m;
-        const int s = (int)(((long long)min(i, S - 1) * n_cand) / S);
+        const int s = S < SMP ? min(i, S - 1)
+                              : (int)(((long long)(i >> 4) * (n_cand - 16)) / (SMP / 16 - 1)) + (i & 15);
         const uint4* p = reinterpret_cast<const uint4*>(k_b + (size_t)s * DI + 32 * kb);
         x0[f] = p[0];
         x1[f] = p[1];

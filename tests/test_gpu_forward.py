@@ -177,7 +177,8 @@ def test_decode_selection_fallback_few_candidates():
     wl = WORKLOADS["decode_128k"].with_(B=2, N=8192, q_offset=8191)
     g = make_inputs(wl, seed=10, device=dev)
     n_cand, S = 8192, 1024
-    pos = torch.tensor([(i * n_cand) // S for i in range(S)], device=dev)
+    # the sample: 64 blocks of 16 consecutive keys, block j at j * (n_cand - 16) // 63
+    pos = torch.tensor([(i // 16) * (n_cand - 16) // (S // 16 - 1) + i % 16 for i in range(S)], device=dev)
     for b in range(wl.B):
         g["k_idx"][b, pos] = g["q_idx"][b, 0, 0]          # the query's head-0 codes
         g["k_idx_scale"][b, pos] = g["q_idx_scale"][b, 0, 0] * 4

@@ -12,7 +12,7 @@ the attention's exact-max rerun is capped at one.
 Per batch entry of each case:
   b = 0  clean;
   b = 1  one NaN code (0x7F) in every query row's head 2;
-  b = 2  NaN codes (0xFF) in 300 keys, some of them at the sampled
+  b = 2  NaN codes (0xFF) in ~300 keys, some of them at the sampled
          positions of the decode threshold;
   b = 3  NaN in one bf16 query element per row and in two latent rows.
 Checks: canary guards around out, lse, idx and the workspace; each idx row
@@ -90,12 +90,15 @@ def test_nan_inputs_through_forward(name, kw):
     p = {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in g.items()}
     # b = 1: a NaN code in head 2 of every query row
     p["q_idx"].view(torch.uint8)[1, :, 2, 7] = 0x7F
-    # b = 2: NaN codes in 300 keys, including positions a sample of the row
-    # is likely to read (its first and last key, evenly spaced ones)
+    # b = 2: NaN codes in ~300 keys: random ones, evenly spaced ones (the
+    # first and last key among them) and keys the decode sample reads (in
+    # blocks 0, 21, 42 and 63 of its 64 blocks of 16 keys, block j at
+    # j * (N - 16) // 63)
     N = wl.N
     rng = np.random.default_rng(12)
-    bad = np.unique(np.concatenate([rng.choice(N, 260, replace=False),
-                                    np.linspace(0, N - 1, 40).astype(np.int64)]))
+    sampled = [j * (N - 16) // 63 + o for j in (0, 21, 42, 63) for o in (0, 7, 15)]
+    bad = np.unique(np.concatenate([rng.choice(N, 250, replace=False),
+                                    np.linspace(0, N - 1, 40).astype(np.int64), np.array(sampled)]))
     p["k_idx"].view(torch.uint8)[2, torch.as_tensor(bad, device=dev), 0] = 0xFF
     # b = 3: NaN in one query element per row and in two latent rows
     p["q"][3, :, 5, 3] = float("nan")
