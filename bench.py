@@ -727,8 +727,10 @@ def run_workload(wl, args, dev, measured, cpu_budget, with_next=True, cpu_rows=N
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # untimed steps first: after a few the clocks have not settled yet (the
+    # decode step times ~5 % slower after 3 warm-up steps than after 50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
